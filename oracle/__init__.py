@@ -1,0 +1,227 @@
+"""FP64 CPU oracle for NVFP4 compressed-latent sparse-MLA decode (ctypes binding of mla_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline leg of the benchmark
+are the only callers.  Nothing in the GPU path imports this package, and this package imports
+nothing from the GPU path.
+
+Each function documents the passage it follows; mla_oracle.c's header lists the pages and the
+readings taken where they are silent.  Arrays cross the boundary as numpy arrays on the host:
+bf16 values travel as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "libmla_oracle.so")
+
+LATENT, ROPE, QK, PAGE = 512, 64, 576, 64
+NVFP4_ROW_BYTES, FP8_ROW_BYTES = 352, 576
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"],
+                   check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32, d = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    sig = {
+        "mlo_bf16_value": (d, [ctypes.c_uint16]),
+        "mlo_e4m3_value": (d, [ctypes.c_uint32]),
+        "mlo_e2m1_value": (d, [ctypes.c_uint32]),
+        "mlo_e4m3_encode_bf16": (ctypes.c_uint32, [ctypes.c_uint16]),
+        "mlo_scale_code": (ctypes.c_uint32, [d]),
+        "mlo_e2m1_encode": (ctypes.c_uint32, [ctypes.c_uint16, ctypes.c_uint32]),
+        "mlo_e2m1_encode_bulk": (None, [P, i64, ctypes.c_uint32, P]),
+        "mlo_e4m3_encode_bulk": (None, [P, i64, P]),
+        "mlo_scale_code_bulk": (None, [P, i64, P]),
+        "mlo_quant_row_nvfp4": (None, [P, P, P]),
+        "mlo_quant_row_fp8": (None, [P, P, P]),
+        "mlo_dequant_row_nvfp4": (None, [P, P]),
+        "mlo_dequant_row_fp8": (None, [P, P]),
+        "mlo_kv_quant_nvfp4": (i64, [P, i64, P, i64, P, i64, P, i64, i64]),
+        "mlo_kv_quant_fp8": (i64, [P, i64, P, i64, P, i64, P, i64, i64]),
+        "mlo_sparse_decode": (i32, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, d, i32, P, i64, P, P, i32]),
+        "mlo_dense_decode_fp8": (i32, [P, P, i64, i64, P, i64, P, i32, i32, i32, d, i32, P, i64, P, P, i32]),
+        "mlo_merge_partials": (None, [P, P, i32, i32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+# --------------------------------------------------------------------------- value definitions
+
+def bf16_value(bits) -> float:
+    return _load().mlo_bf16_value(int(bits))
+
+
+def e4m3_value(code) -> float:
+    """E4M3FN byte -> value (TokenSpeed write-up, MLA KV layout: torch.float8_e4m3fn, max 448)."""
+    return _load().mlo_e4m3_value(int(code))
+
+
+def e2m1_value(code) -> float:
+    """e2m1 nibble -> value (launch post, NVFP4 KV compression: four bits per value)."""
+    return _load().mlo_e2m1_value(int(code))
+
+
+def e4m3_encode(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> E4M3FN bytes, nearest finite, ties to even, saturating at +-448."""
+    x = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(x.shape, np.uint8)
+    _load().mlo_e4m3_encode_bulk(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def scale_code(amax_bits: np.ndarray) -> np.ndarray:
+    """Block amax (bf16 bits, sign ignored) -> E4M3 scale byte nearest to amax/6."""
+    x = np.ascontiguousarray(amax_bits, dtype=np.uint16)
+    out = np.empty(x.shape, np.uint8)
+    _load().mlo_scale_code_bulk(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(bits: np.ndarray, scale: int) -> np.ndarray:
+    """bf16 bits -> e2m1 nibbles under one scale byte (nearest grid point of |x|/s, ties even)."""
+    x = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(x.shape, np.uint8)
+    _load().mlo_e2m1_encode_bulk(_ptr(x), x.size, int(scale), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------- rows
+
+def quant_row_nvfp4(latent_bits: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
+    """One token -> 352-byte row (launch post, NVFP4 KV compression; analysis, row table)."""
+    lat = np.ascontiguousarray(latent_bits, dtype=np.uint16).reshape(LATENT)
+    rope = np.ascontiguousarray(rope_bits, dtype=np.uint16).reshape(ROPE)
+    row = np.zeros(NVFP4_ROW_BYTES, np.uint8)
+    _load().mlo_quant_row_nvfp4(_ptr(lat), _ptr(rope), _ptr(row))
+    return row
+
+
+def quant_row_fp8(latent_bits: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
+    """One token -> 576-byte FP8 row (analysis, row table: no per-row scale)."""
+    lat = np.ascontiguousarray(latent_bits, dtype=np.uint16).reshape(LATENT)
+    rope = np.ascontiguousarray(rope_bits, dtype=np.uint16).reshape(ROPE)
+    row = np.zeros(FP8_ROW_BYTES, np.uint8)
+    _load().mlo_quant_row_fp8(_ptr(lat), _ptr(rope), _ptr(row))
+    return row
+
+
+def dequant_row_nvfp4(row: np.ndarray) -> np.ndarray:
+    r = np.ascontiguousarray(row, dtype=np.uint8).reshape(NVFP4_ROW_BYTES)
+    K = np.empty(QK, np.float64)
+    _load().mlo_dequant_row_nvfp4(_ptr(r), _ptr(K))
+    return K
+
+
+def dequant_row_fp8(row: np.ndarray) -> np.ndarray:
+    r = np.ascontiguousarray(row, dtype=np.uint8).reshape(FP8_ROW_BYTES)
+    K = np.empty(QK, np.float64)
+    _load().mlo_dequant_row_fp8(_ptr(r), _ptr(K))
+    return K
+
+
+# --------------------------------------------------------------------------- pool writers
+
+def kv_quant(fmt: str, k_nope: np.ndarray, k_rope: np.ndarray, slot_mapping: np.ndarray, pool: np.ndarray,
+             page_stride: int, num_pages: int) -> int:
+    """Quantize-on-write into a paged pool (TokenSpeed write-up, MLA KV layout: rows written at slot
+    indices).  k_nope bf16 bits [N,512], k_rope [N,64], slot_mapping int64 [N]; pool uint8 flat array
+    modified in place.  Returns the number of rows written."""
+    kn = np.ascontiguousarray(k_nope, dtype=np.uint16)
+    kr = np.ascontiguousarray(k_rope, dtype=np.uint16)
+    sl = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    n = sl.shape[0]
+    assert kn.shape == (n, LATENT) and kr.shape == (n, ROPE)
+    row_bytes = NVFP4_ROW_BYTES if fmt == "nvfp4" else FP8_ROW_BYTES
+    assert page_stride >= PAGE * row_bytes and pool.size >= num_pages * page_stride
+    f = _load().mlo_kv_quant_nvfp4 if fmt == "nvfp4" else _load().mlo_kv_quant_fp8
+    return f(_ptr(kn), LATENT, _ptr(kr), ROPE, _ptr(sl), n, _ptr(pool), page_stride, num_pages)
+
+
+# --------------------------------------------------------------------------- attention
+
+def sparse_decode(q, pool, page_stride, num_pages, block_table, ctx, indices, sm_scale, causal=False, units=None,
+                  nthreads=0):
+    """Sparse decode (launch post, native NVFP4 sparse MLA decode kernel): q bf16 bits [B,T,H,576];
+    indices int32 [B,T,k] of logical positions (-1 = unused).  Returns (out [n,H,512], lse [n,H], threads)
+    in float64, n = B*T or len(units)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, T, H, D = q.shape
+    assert D == QK
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    k = idx.shape[2]
+    assert idx.shape[:2] == (B, T)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cx = np.ascontiguousarray(ctx, dtype=np.int32)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int64)
+    n = B * T if un is None else un.size
+    out = np.empty((n, H, LATENT), np.float64)
+    lse = np.empty((n, H), np.float64)
+    used = _load().mlo_sparse_decode(_ptr(q), _ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx),
+                                     _ptr(idx), B, T, H, k, float(sm_scale), int(bool(causal)), _ptr(un),
+                                     0 if un is None else un.size, _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse, used
+
+
+def dense_decode_fp8(q, pool, page_stride, num_pages, block_table, ctx, sm_scale, causal=False, units=None,
+                     nthreads=0):
+    """Dense decode over a 576-byte FP8 row cache (the FP8 attention the launch post compares with):
+    every position up to the limit is attended."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, T, H, D = q.shape
+    assert D == QK
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cx = np.ascontiguousarray(ctx, dtype=np.int32)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int64)
+    n = B * T if un is None else un.size
+    out = np.empty((n, H, LATENT), np.float64)
+    lse = np.empty((n, H), np.float64)
+    used = _load().mlo_dense_decode_fp8(_ptr(q), _ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1],
+                                        _ptr(cx), B, T, H, float(sm_scale), int(bool(causal)), _ptr(un),
+                                        0 if un is None else un.size, _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse, used
+
+
+def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """LSE-weighted merge of S partial results of one query token (launch post: the blocks of a
+    cluster merge their partial results).  o_parts [S,H,512], lse_parts [S,H] -> (out [H,512], lse [H])."""
+    o = np.ascontiguousarray(o_parts, dtype=np.float64)
+    l = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    S, H, _ = o.shape
+    out = np.empty((H, LATENT), np.float64)
+    lse = np.empty(H, np.float64)
+    _load().mlo_merge_partials(_ptr(o), _ptr(l), S, H, _ptr(out), _ptr(lse))
+    return out, lse

@@ -1,0 +1,500 @@
+"""Pins of the FP64 oracle against things other than itself (CPU only).
+
+Each test names what fixes the expected value: a figure printed on the pages (tests/golden/, cited
+there), a library routine (torch's float8 decoders and casts), exact rational arithmetic, a second
+independent algorithm, or a mathematical invariant of softmax attention.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+FINITE_BF16 = np.array([b for b in range(65536) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_f64(bits):
+    return W.bf16_to_f32(bits).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- generic minifloat decoder
+def minifloat(code, ebits, mbits, bias):
+    """Sign / exponent / mantissa decoding with subnormals (no special values)."""
+    s = (code >> (ebits + mbits)) & 1
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    v = (m / (1 << mbits)) * 2.0 ** (1 - bias) if e == 0 else (1 + m / (1 << mbits)) * 2.0 ** (e - bias)
+    return -v if s else v
+
+
+def test_generic_minifloat_matches_torch_float8_formats():
+    # Pins the generic decoder used below against two library formats.
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    e5 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).double().numpy()
+    for c in range(256):
+        if (c & 0x7F) != 0x7F:
+            assert minifloat(c, 4, 3, 7) == e4[c]
+        if ((c >> 2) & 0x1F) != 0x1F:
+            assert minifloat(c, 5, 2, 15) == e5[c]
+
+
+# --------------------------------------------------------------------------- row layout (pages' numbers)
+def test_row_size_closed_form_from_pages():
+    g = _golden("row_layout.json")
+    n, r, grp = g["latent_values"], g["rope_values"], g["values_per_scale"]
+    assert n * 4 // 8 == g["nvfp4"]["latent_bytes"]
+    assert n // grp == g["nvfp4"]["scale_bytes"]
+    assert r == g["nvfp4"]["rope_bytes"]
+    assert sum(g["nvfp4"][k] for k in ("latent_bytes", "scale_bytes", "rope_bytes")) == g["nvfp4"]["row_bytes"] == 352
+    assert g["fp8"]["latent_bytes"] + g["fp8"]["rope_bytes"] == g["fp8"]["row_bytes"] == 576
+    assert round(576 / 352, 2) == g["row_ratio_printed"]
+    rng = np.random.default_rng(0)
+    lat, rope = W.gen_latent_rope(rng, 1)
+    assert oracle.quant_row_nvfp4(lat[0], rope[0]).size == g["nvfp4"]["row_bytes"]
+    assert oracle.quant_row_fp8(lat[0], rope[0]).size == g["fp8"]["row_bytes"]
+    assert oracle.NVFP4_ROW_BYTES == 352 and oracle.FP8_ROW_BYTES == 576
+
+
+def test_pool_placement_rows_at_352_byte_stride():
+    # Rows of one page sit back to back; pages at page_stride; negative / out-of-pool slots skipped.
+    rng = np.random.default_rng(1)
+    lat, rope = W.gen_latent_rope(rng, 5)
+    page_stride = 64 * 352 + 160  # a padded page stride (block-major pools have larger strides)
+    pool = np.zeros(3 * page_stride, np.uint8)
+    slots = np.array([0, 1, 64 + 63, -1, 3 * 64], np.int64)
+    n = oracle.kv_quant("nvfp4", lat, rope, slots, pool, page_stride, 3)
+    assert n == 3
+    assert np.array_equal(pool[0:352], oracle.quant_row_nvfp4(lat[0], rope[0]))
+    assert np.array_equal(pool[352:704], oracle.quant_row_nvfp4(lat[1], rope[1]))
+    assert np.array_equal(pool[page_stride + 63 * 352: page_stride + 64 * 352], oracle.quant_row_nvfp4(lat[2], rope[2]))
+    written = np.zeros_like(pool, dtype=bool)
+    written[0:704] = True
+    written[page_stride + 63 * 352: page_stride + 64 * 352] = True
+    assert not pool[~written].any()
+
+
+def test_constants_from_pages():
+    g = _golden("constants.json")
+    # the printed softmax scale is 1/sqrt(192) (192 = 128 + 64) to the 7 digits shown
+    assert abs(1 / math.sqrt(192) - g["softmax_scale_printed"]) < 5e-8
+    assert W.CONFIGS["sparse"].sm_scale == pytest.approx(g["softmax_scale_printed"], abs=5e-8)
+    assert oracle.e4m3_value(0x7E) == g["e4m3_max"]
+    assert W.PAGE == g["page_size"] and W.CONFIGS["sparse"].topk == g["index_topk"]
+
+
+# --------------------------------------------------------------------------- decoders
+def test_e4m3_decode_all_codes_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(v)
+        else:
+            assert v == ref[c], c
+    assert max(abs(oracle.e4m3_value(c)) for c in range(256) if (c & 0x7F) != 0x7F) == 448.0
+
+
+def test_e2m1_decode_all_codes_vs_generic_minifloat():
+    # e2m1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit, no special values
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    assert vals == [minifloat(c, 2, 1, 1) for c in range(16)]
+    assert sorted(set(abs(v) for v in vals)) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_bf16_decode_vs_torch():
+    ref = torch.from_numpy(FINITE_BF16.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_value(b) for b in FINITE_BF16[::97]])
+    assert np.array_equal(got, ref[::97])
+
+
+# --------------------------------------------------------------------------- encoders
+def _threshold_e2m1(a, s):
+    """Nearest e2m1 magnitude code of a/s by counting crossed midpoints (ties to even code)."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * s
+    code = np.zeros(a.shape, np.int64)
+    for k, t in enumerate(mids):
+        code += (a > t) | ((a == t) & (k % 2 == 1))
+    return code
+
+
+def test_e2m1_encode_exhaustive_vs_threshold_method():
+    # every finite bf16 value x every positive finite E4M3 scale (about 8.2M pairs)
+    x = FINITE_BF16
+    a = np.abs(_bf16_f64(x))
+    sign = (x >> 15).astype(np.int64)
+    for sc in range(1, 0x7F):
+        s = oracle.e4m3_value(sc)
+        got = oracle.e2m1_encode(x, sc).astype(np.int64)
+        want = _threshold_e2m1(a, s) | (sign << 3)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (sc, x[bad[:5]], got[bad[:5]], want[bad[:5]])
+    # zero scale: magnitude 0, sign kept
+    got0 = oracle.e2m1_encode(x, 0).astype(np.int64)
+    assert np.array_equal(got0, sign << 3)
+
+
+def test_e2m1_encode_exact_rational_sample():
+    rng = np.random.default_rng(5)
+    grid = [Fraction(v) for v in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    xs = rng.choice(FINITE_BF16, 4000)
+    scs = rng.integers(1, 0x7F, 4000)
+    for xb, sc in zip(xs, scs):
+        a = abs(Fraction(oracle.bf16_value(int(xb))))
+        s = Fraction(oracle.e4m3_value(int(sc)))
+        r = a / s
+        d = [abs(r - g) for g in grid]
+        best = min(range(8), key=lambda k: (d[k], k % 2))
+        got = oracle.e2m1_encode(np.array([xb], np.uint16), int(sc))[0]
+        assert got & 7 == best and (got >> 3) == (int(xb) >> 15)
+
+
+def test_scale_code_all_bf16_amax_vs_torch_cast():
+    pos = FINITE_BF16[(FINITE_BF16 >> 15) == 0]
+    amax = _bf16_f64(pos)
+    got = oracle.scale_code(pos).astype(np.int64)
+    r = amax / 6.0
+    ref = torch.from_numpy(np.minimum(r, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    assert np.array_equal(got, ref)
+
+
+def test_scale_code_exact_rational_sample_and_ties():
+    rng = np.random.default_rng(6)
+    pos = FINITE_BF16[(FINITE_BF16 >> 15) == 0]
+    cand = [(c, Fraction(oracle.e4m3_value(c))) for c in range(0x7F)]
+    # includes every amax that sits exactly on a midpoint x 6 (the tie cases)
+    mids = set()
+    for c in range(0x7E):
+        m6 = (cand[c][1] + cand[c + 1][1]) / 2 * 6
+        mids.add(float(m6))
+    tie_bits = [b for b in pos if oracle.bf16_value(int(b)) in mids]
+    assert len(tie_bits) > 50
+    sample = list(rng.choice(pos, 3000)) + tie_bits
+    for b in sample:
+        r = Fraction(oracle.bf16_value(int(b))) / 6
+        best = min(cand, key=lambda cv: (abs(r - cv[1]), cv[0] % 2))[0]
+        assert oracle.scale_code(np.array([b], np.uint16))[0] == best, b
+
+
+def test_e4m3_encode_all_bf16_vs_torch_cast_and_saturation():
+    x = FINITE_BF16
+    v = _bf16_f64(x)
+    got = oracle.e4m3_encode(x).astype(np.int64)
+    inside = np.abs(v) <= 448.0
+    ref = torch.from_numpy(v[inside]).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    assert np.array_equal(got[inside], ref)
+    sign = (x[~inside] >> 15).astype(np.int64)
+    assert np.array_equal(got[~inside], 0x7E | (sign << 7))
+
+
+def test_round_trip_of_representable_values():
+    # decode(encode(decode(c))) == decode(c)
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        v = oracle.e4m3_value(c)
+        bits = W.bf16_bits(np.array([v], np.float32))  # every E4M3 value is exact in bf16
+        assert W.bf16_to_f32(bits)[0] == v
+        assert oracle.e4m3_value(int(oracle.e4m3_encode(bits)[0])) == v
+    one = 0x38  # scale 1.0
+    assert oracle.e4m3_value(one) == 1.0
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        bits = W.bf16_bits(np.array([v], np.float32))
+        assert oracle.e2m1_value(int(oracle.e2m1_encode(bits, one)[0])) == v
+
+
+# --------------------------------------------------------------------------- row quantization properties
+def _split(row):
+    nib = np.empty(512, np.int64)
+    nib[0::2] = row[:256] & 15
+    nib[1::2] = row[:256] >> 4
+    return nib, row[256:288].astype(np.int64), row[288:352]
+
+
+def test_row_error_bound_and_grid():
+    rng = np.random.default_rng(7)
+    lat, rope = W.gen_latent_rope(rng, 64)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for r in range(64):
+        row = oracle.quant_row_nvfp4(lat[r], rope[r])
+        x = _bf16_f64(lat[r])
+        K = oracle.dequant_row_nvfp4(row)
+        nib, sc, _ = _split(row)
+        s = np.array([oracle.e4m3_value(c) for c in sc]).repeat(16)
+        # dequantized value = e2m1 value x block scale
+        assert np.array_equal(K[:512], np.array([oracle.e2m1_value(c) for c in nib]) * s)
+        # nearest grid point: no other grid point is closer to x/s
+        a = np.abs(x) / s
+        assert np.all(np.abs(a - np.abs(K[:512]) / s) <= np.min(np.abs(a[:, None] - grid[None, :]), axis=1) + 0)
+        # block scale is the E4M3 value nearest to amax/6
+        amax = np.abs(x).reshape(32, 16).max(1)
+        for j in range(32):
+            d = [abs(amax[j] / 6 - oracle.e4m3_value(c)) for c in range(0x7F)]
+            assert abs(amax[j] / 6 - oracle.e4m3_value(int(sc[j]))) == min(d)
+        # rope: E4M3 cast without scale
+        ref_rope = torch.from_numpy(_bf16_f64(rope[r])).to(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(K[512:], ref_rope)
+
+
+def test_power_of_two_and_sign_equivariance():
+    rng = np.random.default_rng(8)
+    lat, rope = W.gen_latent_rope(rng, 16)
+    tested = 0
+    for r in range(16):
+        x = W.bf16_to_f32(lat[r])
+        base = oracle.quant_row_nvfp4(lat[r], rope[r])
+        nib0, sc0, _ = _split(base)
+        if sc0.min() < 0x10 or sc0.max() > 0x6E:  # scales stay normal and below 448 after the shift
+            continue
+        tested += 1
+        for k in (-1, 1, 2):
+            row = oracle.quant_row_nvfp4(W.bf16_bits(x * np.float32(2.0 ** k)), rope[r])
+            nib, sc, _ = _split(row)
+            assert np.array_equal(nib, nib0)
+            assert np.array_equal(sc, sc0 + 8 * k)  # exponent field moves by k
+        neg = oracle.quant_row_nvfp4(lat[r] ^ np.uint16(0x8000), rope[r])
+        nibn, scn, _ = _split(neg)
+        assert np.array_equal(scn, sc0)
+        assert np.array_equal(nibn, nib0 ^ 8)
+    assert tested >= 8
+
+
+def test_zero_and_tiny_blocks():
+    lat = np.zeros(512, np.uint16)
+    lat[16:32] = 0x8000  # negative zeros keep their sign bit
+    lat[32] = W.bf16_bits(np.array([6 * 2.0 ** -10], np.float32))[0]  # amax/6 = 2^-10: tie -> code 0
+    lat[48] = W.bf16_bits(np.array([6 * 2.0 ** -10 * 1.0078125], np.float32))[0]  # just above the tie
+    row = oracle.quant_row_nvfp4(lat, np.zeros(64, np.uint16))
+    nib, sc, rope = _split(row)
+    assert sc[0] == 0 and not nib[:16].any()
+    assert sc[1] == 0 and np.all(nib[16:32] == 8)
+    assert sc[2] == 0 and nib[32] == 0
+    assert sc[3] == 1 and nib[48] == 5  # smallest subnormal scale 2^-9; |x|/s ~ 3.02 -> 3
+    assert not rope.any()
+
+
+def test_saturation_of_large_values():
+    lat = np.zeros(512, np.uint16)
+    lat[0] = W.bf16_bits(np.array([1e6], np.float32))[0]
+    lat[1] = W.bf16_bits(np.array([-3e5], np.float32))[0]
+    rope = W.bf16_bits(np.full(64, -1e4, np.float32))
+    row = oracle.quant_row_nvfp4(lat, rope)
+    nib, sc, rp = _split(row)
+    assert sc[0] == 0x7E and nib[0] == 7 and nib[1] == 15
+    assert np.all(rp == 0xFE)
+
+
+# --------------------------------------------------------------------------- attention
+def _small_case(seed, B=2, T=1, H=4, L=300, topk=64, causal=False, fmt="nvfp4"):
+    rng = np.random.default_rng(seed)
+    cfg = W.DecodeConfig("t", B=B, T=T, H=H, topk=topk, fmt=fmt, ctx=L, causal=causal, seed=seed)
+    lay = W.gen_layout(cfg, rng)
+    pool = np.zeros(lay.num_pages * cfg.page_stride, np.uint8)
+    src = {}
+    for b in range(B):
+        pos = np.arange(int(lay.ctx[b]))
+        lat, rope = W.gen_latent_rope(rng, pos.size)
+        oracle.kv_quant(fmt, lat, rope, W.slots_for_request(lay, b, pos), pool, cfg.page_stride, lay.num_pages)
+        src[b] = (lat, rope)
+    q = W.gen_q(rng, B, T, H)
+    idx = W.gen_indices(rng, lay.ctx, T, topk, causal) if topk else None
+    return cfg, lay, pool, q, idx, rng
+
+
+def _rows_of(cfg, lay, pool, b, positions):
+    rb = cfg.row_bytes
+    out = []
+    for p in positions:
+        page = lay.block_table[b, p // 64]
+        off = page * cfg.page_stride + (p % 64) * rb
+        out.append(pool[off:off + rb])
+    return out
+
+
+def _independent_K(row, fmt):
+    """Dequantize with the test's own decoders: torch float8 for E4M3, the generic minifloat for e2m1."""
+    f8 = torch.from_numpy(np.ascontiguousarray(row)).view(torch.float8_e4m3fn).double().numpy()
+    if fmt == "fp8":
+        return f8
+    nib = np.empty(512, np.int64)
+    nib[0::2] = row[:256] & 15
+    nib[1::2] = row[:256] >> 4
+    e2 = np.array([minifloat(int(c), 2, 1, 1) for c in nib])
+    return np.concatenate([e2 * f8[256:288].repeat(16), f8[288:352]])
+
+
+def _independent_attention(qbits, K, sm_scale):
+    """Softmax attention via log-sum-exp in numpy."""
+    from scipy.special import logsumexp
+    q = _bf16_f64(qbits)  # [H,576]
+    z = sm_scale * (q @ K.T)  # [H,n]
+    lse = logsumexp(z, axis=1)
+    P = np.exp(z - lse[:, None])
+    return P @ K[:, :512], lse
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_full_selection_equals_independent_attention(fmt):
+    cfg, lay, pool, q, _, _ = _small_case(11, L=200, topk=0, fmt=fmt)
+    positions = np.arange(200)
+    idx = np.tile(np.random.default_rng(3).permutation(positions).astype(np.int32), (cfg.B, 1, 1)).reshape(cfg.B, 1, 200)
+    for b in range(cfg.B):
+        K = np.stack([_independent_K(r, fmt) for r in _rows_of(cfg, lay, pool, b, positions)])
+        ref_o, ref_l = _independent_attention(q[b, 0], K, cfg.sm_scale)
+        if fmt == "nvfp4":
+            out, lse, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, idx,
+                                               cfg.sm_scale)
+        else:
+            out, lse, _ = oracle.dense_decode_fp8(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx,
+                                                  cfg.sm_scale)
+        np.testing.assert_allclose(out[b], ref_o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse[b], ref_l, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_selected_v():
+    cfg, lay, pool, q, idx, _ = _small_case(12)
+    q[:] = 0
+    out, lse, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, idx,
+                                       cfg.sm_scale)
+    for b in range(cfg.B):
+        V = np.stack([_independent_K(r, "nvfp4")[:512] for r in _rows_of(cfg, lay, pool, b, idx[b, 0])])
+        np.testing.assert_allclose(out[b], np.broadcast_to(V.mean(0), out[b].shape), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[b], math.log(idx.shape[2]), rtol=1e-13)
+
+
+def test_identical_keys_give_mean_of_v():
+    # q_nope = 0 and every selected row has the same rope part: all scores equal although latents differ
+    rng = np.random.default_rng(13)
+    H, n = 4, 40
+    lat, rope = W.gen_latent_rope(rng, n)
+    rope[:] = rope[0]
+    pool = np.zeros(64 * 352 * 2, np.uint8)
+    bt = np.array([[1]], np.int32)
+    oracle.kv_quant("nvfp4", lat, rope, 64 + np.arange(n), pool, 64 * 352, 2)
+    q = W.gen_q(rng, 1, 1, H)
+    q[..., :512] = 0
+    idx = rng.permutation(n).astype(np.int32).reshape(1, 1, n)
+    out, _, _ = oracle.sparse_decode(q, pool, 64 * 352, 2, bt, np.array([n], np.int32), idx, 0.07)
+    V = np.stack([oracle.dequant_row_nvfp4(pool[(64 + i) * 352:(65 + i) * 352])[:512] for i in range(n)])
+    assert np.abs(V - V[0]).max() > 0.1
+    np.testing.assert_allclose(out[0], np.broadcast_to(V.mean(0), (H, 512)), rtol=1e-12, atol=1e-13)
+
+
+def test_single_index_gives_that_row():
+    cfg, lay, pool, q, idx, _ = _small_case(14)
+    one = np.full_like(idx, -1)
+    one[:, :, 7] = idx[:, :, 0]
+    out, lse, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, one,
+                                       cfg.sm_scale)
+    for b in range(cfg.B):
+        K = _independent_K(_rows_of(cfg, lay, pool, b, [idx[b, 0, 0]])[0], "nvfp4")
+        assert np.array_equal(out[b], np.broadcast_to(K[:512], out[b].shape))
+        np.testing.assert_allclose(lse[b], cfg.sm_scale * (_bf16_f64(q[b, 0]) @ K), rtol=1e-13)
+
+
+def test_permutation_and_padding_invariance():
+    cfg, lay, pool, q, idx, rng = _small_case(15)
+    args = (cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx)
+    out0, lse0, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale)
+    perm = idx[:, :, rng.permutation(idx.shape[2])]
+    out1, lse1, _ = oracle.sparse_decode(q, pool, *args, perm, cfg.sm_scale)
+    pad = np.full((cfg.B, 1, idx.shape[2] + 50), -1, np.int32)
+    where = np.sort(rng.choice(pad.shape[2], idx.shape[2], replace=False))
+    pad[:, :, where] = idx
+    out2, lse2, _ = oracle.sparse_decode(q, pool, *args, pad, cfg.sm_scale)
+    for o, l in ((out1, lse1), (out2, lse2)):
+        np.testing.assert_allclose(o, out0, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l, lse0, rtol=1e-13)
+
+
+def test_split_and_merge_equals_unsplit():
+    cfg, lay, pool, q, idx, rng = _small_case(16, topk=100)
+    args = (cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx)
+    out0, lse0, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale)
+    for S in (2, 3, 7):
+        parts_o, parts_l = [], []
+        bounds = np.linspace(0, idx.shape[2], S + 1).astype(int)
+        for s in range(S):
+            sub = np.full_like(idx, -1)
+            sub[:, :, bounds[s]:bounds[s + 1]] = idx[:, :, bounds[s]:bounds[s + 1]]
+            o, l, _ = oracle.sparse_decode(q, pool, *args, sub, cfg.sm_scale)
+            parts_o.append(o)
+            parts_l.append(l)
+        for b in range(cfg.B):
+            mo, ml = oracle.merge_partials(np.stack([p[b] for p in parts_o]), np.stack([p[b] for p in parts_l]))
+            np.testing.assert_allclose(mo, out0[b], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(ml, lse0[b], rtol=1e-13)
+    # an empty part (lse = -inf) carries no weight; all-empty gives 0 / -inf
+    mo, ml = oracle.merge_partials(np.stack([out0[0], np.zeros_like(out0[0])]),
+                                   np.stack([lse0[0], np.full_like(lse0[0], -np.inf)]))
+    np.testing.assert_allclose(mo, out0[0], rtol=1e-14)
+    mo, ml = oracle.merge_partials(np.zeros((2, cfg.H, 512)), np.full((2, cfg.H), -np.inf))
+    assert not mo.any() and np.all(ml == -np.inf)
+
+
+def test_causal_limit_and_invalid_entries_are_ignored():
+    cfg, lay, pool, q, idx, rng = _small_case(17, T=4, L=257, topk=80, causal=True)
+    args = (cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx)
+    out0, lse0, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale, causal=True)
+    # entries past each token's limit, past the context, or < -1 behave as absent
+    bad = idx.copy()
+    L = int(lay.ctx[0])
+    extra = np.full((cfg.B, cfg.T, 5), -1, np.int32)
+    for t in range(cfg.T):
+        extra[:, t, :] = [L - cfg.T + t + 1 if t < cfg.T - 1 else L, L + 10, -7, 10 ** 6, -1]
+    bad = np.concatenate([bad, extra], axis=2)
+    out1, lse1, _ = oracle.sparse_decode(q, pool, *args, bad, cfg.sm_scale, causal=True)
+    np.testing.assert_allclose(out1, out0, rtol=1e-12, atol=1e-13)
+    # a page-table entry outside the pool removes the positions on that page
+    bt = lay.block_table.copy()
+    bt[0, 1] = lay.num_pages + 3
+    keep = idx.copy()
+    keep[0][(keep[0] // 64) == 1] = -1
+    out2, _, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, bt, lay.ctx, idx, cfg.sm_scale,
+                                      causal=True)
+    out3, _, _ = oracle.sparse_decode(q, pool, *args, keep, cfg.sm_scale, causal=True)
+    np.testing.assert_allclose(out2, out3, rtol=1e-12, atol=1e-13)
+
+
+def test_empty_selection():
+    cfg, lay, pool, q, idx, _ = _small_case(18)
+    none = np.full_like(idx, -1)
+    out, lse, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, none,
+                                       cfg.sm_scale)
+    assert not out.any() and np.all(lse == -np.inf)
+
+
+def test_dense_equals_sparse_over_full_list_on_same_rows():
+    # dense FP8 decode and sparse decode agree in definition: same positions, same rows -> same result
+    cfg, lay, pool, q, _, _ = _small_case(19, L=150, topk=0, fmt="fp8", T=2, causal=True)
+    out_d, lse_d, _ = oracle.dense_decode_fp8(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx,
+                                              cfg.sm_scale, causal=True)
+    for b in range(cfg.B):
+        for t in range(cfg.T):
+            lim = 150 - 2 + t
+            K = np.stack([_independent_K(r, "fp8") for r in _rows_of(cfg, lay, pool, b, np.arange(lim + 1))])
+            ro, rl = _independent_attention(q[b, t], K, cfg.sm_scale)
+            np.testing.assert_allclose(out_d[b * cfg.T + t], ro, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse_d[b * cfg.T + t], rl, rtol=1e-12)
+
+
+def test_units_subset_matches_full_run():
+    cfg, lay, pool, q, idx, _ = _small_case(20, B=3, T=2, causal=True)
+    args = (cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx)
+    out, lse, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale, causal=True)
+    units = np.array([5, 0, 3], np.int64)
+    out_u, lse_u, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale, causal=True, units=units)
+    assert np.array_equal(out_u, out[units]) and np.array_equal(lse_u, lse[units])

@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for NVFP4 sparse-MLA decode: shapes, value distributions and structure only.
+
+This module holds none of the method's arithmetic (no quantization, no attention).  The oracle and
+the HIP path both take what it produces; neither imports the other.
+
+Recipe (the pages' workload is agent-session replay on a trained model, which is not available here;
+these inputs stand in for it with the pages' shapes):
+  * latent  x = N(0,1) * r_row, r_row ~ lognormal(0, 0.5) per token row, each element x8 with
+    probability 0.01, rounded to bf16 (round to nearest even);
+  * rope    N(0,1) -> bf16;
+  * q       N(0,1) -> bf16, shape [B, T, H, 576];
+  * indices per query token: topk distinct positions drawn uniformly without replacement from
+    [0, limit], in random order, int32 (limit = L-1, or L-T+t under the causal rule); when the limit
+    leaves fewer than topk positions the rest is -1;
+  * page table: the ceil(L/64) logical pages of every request map to a random permutation of the
+    physical pages; physical page 0 is a pad page no request uses; unused table entries are -1.
+CPU generators use numpy PCG64; device generators use a seeded torch generator on the GPU.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+LATENT, ROPE, QK, PAGE = 512, 64, 576, 64
+NVFP4_ROW_BYTES, FP8_ROW_BYTES = 352, 576
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    B: int
+    T: int
+    H: int
+    topk: int            # 0 = dense (every position up to the limit)
+    fmt: str             # "nvfp4" (352-byte rows) or "fp8" (576-byte rows)
+    ctx: int = 0         # fixed context length, or 0 when ctx_range is used
+    ctx_range: tuple = ()  # (lo, hi): log-uniform context lengths
+    causal: bool = False
+    quant_chunk: int = 0  # tokens quantized into free slots as part of the step
+    alloc_tokens: int = 0  # per-request allocation when larger than the used context
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def row_bytes(self) -> int:
+        return NVFP4_ROW_BYTES if self.fmt == "nvfp4" else FP8_ROW_BYTES
+
+    @property
+    def page_stride(self) -> int:
+        return PAGE * self.row_bytes
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(192.0)
+
+
+CONFIGS = {
+    "tiny": DecodeConfig("tiny", B=2, T=1, H=16, topk=256, fmt="nvfp4", ctx=4096, seed=20260001),
+    "dense_b4": DecodeConfig("dense_b4", B=4, T=1, H=128, topk=0, fmt="fp8", ctx=8192, seed=20260002),
+    "dense_b8": DecodeConfig("dense_b8", B=8, T=1, H=128, topk=0, fmt="fp8", ctx=8192, seed=20260002),
+    "dense_b16": DecodeConfig("dense_b16", B=16, T=1, H=128, topk=0, fmt="fp8", ctx=8192, seed=20260002),
+    "sparse": DecodeConfig("sparse", B=64, T=1, H=32, topk=2048, fmt="nvfp4", ctx=140000, seed=20260003),
+    "spec": DecodeConfig("spec", B=128, T=4, H=32, topk=2048, fmt="nvfp4", ctx_range=(8192, 146000), causal=True,
+                         seed=20260004),
+    "mixed": DecodeConfig("mixed", B=256, T=1, H=128, topk=2048, fmt="nvfp4", ctx_range=(8192, 146000),
+                          quant_chunk=4096, alloc_tokens=146000, seed=20260005),
+}
+
+
+# --------------------------------------------------------------------------- helpers (input synthesis)
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def context_lengths(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
+    if cfg.ctx:
+        return np.full(cfg.B, cfg.ctx, np.int32)
+    lo, hi = cfg.ctx_range
+    return np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=cfg.B))).astype(np.int32)
+
+
+def gen_latent_rope(rng: np.random.Generator, n: int):
+    """n token rows -> (latent bf16 bits [n,512], rope bf16 bits [n,64])."""
+    r = rng.lognormal(0.0, 0.5, size=(n, 1)).astype(np.float32)
+    x = rng.standard_normal((n, LATENT), dtype=np.float32) * r
+    x = np.where(rng.random((n, LATENT)) < 0.01, x * 8.0, x).astype(np.float32)
+    y = rng.standard_normal((n, ROPE), dtype=np.float32)
+    return bf16_bits(x), bf16_bits(y)
+
+
+def gen_q(rng: np.random.Generator, B: int, T: int, H: int) -> np.ndarray:
+    return bf16_bits(rng.standard_normal((B, T, H, QK), dtype=np.float32))
+
+
+def position_limit(L: int, T: int, t: int, causal: bool) -> int:
+    return L - T + t if causal else L - 1
+
+
+def gen_indices(rng: np.random.Generator, ctx: np.ndarray, T: int, topk: int, causal: bool) -> np.ndarray:
+    B = ctx.shape[0]
+    out = np.full((B, T, topk), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            lim = position_limit(int(ctx[b]), T, t, causal)
+            n = min(topk, lim + 1)
+            if n <= 0:
+                continue
+            sel = rng.choice(lim + 1, size=n, replace=False).astype(np.int32)
+            out[b, t, :n] = sel
+            rng.shuffle(out[b, t])
+    return out
+
+
+@dataclass
+class PoolLayout:
+    ctx: np.ndarray            # int32 [B]
+    block_table: np.ndarray    # int32 [B, max_pages]
+    num_pages: int             # physical pages (page 0 = pad)
+    free_pages: np.ndarray     # physical pages no request uses
+
+
+def gen_layout(cfg: DecodeConfig, rng: np.random.Generator, ctx: np.ndarray | None = None) -> PoolLayout:
+    if ctx is None:
+        ctx = context_lengths(cfg, rng)
+    pages_per = (ctx.astype(np.int64) + PAGE - 1) // PAGE
+    alloc_per = max(int(pages_per.max()), (cfg.alloc_tokens + PAGE - 1) // PAGE if cfg.alloc_tokens else 0)
+    used = int(pages_per.sum())
+    total = 1 + (cfg.B * alloc_per if cfg.alloc_tokens else used)
+    if cfg.quant_chunk and not cfg.alloc_tokens:
+        total += (cfg.quant_chunk + PAGE - 1) // PAGE
+    perm = rng.permutation(np.arange(1, total, dtype=np.int64))
+    bt = np.full((cfg.B, int(pages_per.max())), -1, np.int32)
+    off = 0
+    for b in range(cfg.B):
+        n = int(pages_per[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    return PoolLayout(ctx=ctx.astype(np.int32), block_table=bt, num_pages=int(total), free_pages=perm[off:])
+
+
+def slots_for_request(layout: PoolLayout, b: int, positions: np.ndarray) -> np.ndarray:
+    pages = layout.block_table[b, positions // PAGE].astype(np.int64)
+    return pages * PAGE + (positions % PAGE)
+
+
+def gen_chunk_slots(layout: PoolLayout, rng: np.random.Generator, n: int) -> np.ndarray:
+    """n slots on free pages, spread over the pool (the mixed step's write chunk)."""
+    npg = (n + PAGE - 1) // PAGE
+    pages = rng.choice(layout.free_pages, size=npg, replace=False).astype(np.int64)
+    slots = (pages[:, None] * PAGE + np.arange(PAGE)[None, :]).reshape(-1)[:n]
+    return rng.permutation(slots)
+
+
+# --------------------------------------------------------------------------- device generators (torch)
+
+def torch_bf16_normal(gen, shape, device, scale_rows=False, outliers=False):
+    """Seeded N(0,1) bf16 tensor on the device; with scale_rows, each row (last axis) is multiplied by
+    lognormal(0, 0.5); with outliers, each element is x8 with probability 0.01."""
+    import torch
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if scale_rows:
+        r = torch.empty(shape[:-1] + (1,), device=device, dtype=torch.float32).log_normal_(0.0, 0.5, generator=gen)
+        x = x * r
+    if outliers:
+        m = torch.rand(shape, generator=gen, device=device) < 0.01
+        x = torch.where(m, x * 8.0, x)
+    return x.to(torch.bfloat16)
+
+
+def torch_indices(gen, ctx: np.ndarray, T: int, topk: int, causal: bool, device):
+    """[B,T,topk] int32 on the device: distinct uniform positions in [0, limit], random order, -1 pad."""
+    import torch
+    B = ctx.shape[0]
+    lims = np.array([[position_limit(int(ctx[b]), T, t, causal) for t in range(T)] for b in range(B)], np.int64)
+    Lmax = int(lims.max()) + 1
+    out = torch.empty((B, T, topk), dtype=torch.int32, device=device)
+    lim_t = torch.as_tensor(lims, device=device)
+    pos = torch.arange(Lmax, device=device)
+    rows_per = max(1, (1 << 26) // max(Lmax, 1))
+    flat_lim = lim_t.reshape(-1)
+    flat_out = out.view(-1, topk)
+    for s in range(0, B * T, rows_per):
+        e = min(B * T, s + rows_per)
+        keys = torch.rand((e - s, Lmax), generator=gen, device=device)
+        keys = torch.where(pos[None, :] <= flat_lim[s:e, None], keys, torch.full_like(keys, -1.0))
+        k = min(topk, Lmax)
+        v, i = torch.topk(keys, k, dim=1, sorted=True)
+        i = torch.where(v >= 0, i, torch.full_like(i, -1)).to(torch.int32)
+        if k < topk:
+            i = torch.cat([i, torch.full((e - s, topk - k), -1, dtype=torch.int32, device=device)], dim=1)
+        flat_out[s:e] = i
+    return out
