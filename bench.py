@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of one NVFP4 sparse-MLA decode step on one MI355X.
+
+A step is the whole hot path over one batch: quantize-on-write of the step's new cache rows (the B*T
+query tokens' own rows; for the mixed workload the 4,096-token write chunk) followed by the decode
+(split decode kernel + LSE merge) of the B*T query tokens.  Inputs are seeded synthetic data of the
+workload's shapes, resident in HBM before timing starts.  Eight independent (query, index) sets
+rotate across steps so the 256 MB last-level cache cannot hold the working set.
+
+Prints one JSON line (rank 0).  `roofline` covers the decode call (the dominant work), timed with
+HIP events on its stream inside the timed steps; `cpu_baseline` times the FP64 oracle on the host
+cores over a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+N_SETS = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg, valid_rows: int):
+    """Bytes the method must move per decode call and its MFMA flops (QK^T + PV)."""
+    nq = cfg.B * cfg.T
+    rows_bytes = valid_rows * cfg.row_bytes
+    qo_bytes = nq * cfg.H * (576 * 2 + 512 * 2)
+    list_bytes = (valid_rows * 8) if cfg.topk else 0  # index + page-table entry per selected row
+    flops = 2.0 * (576 + 512) * cfg.H * valid_rows
+    return rows_bytes + qo_bytes + list_bytes, flops
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_compressed_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """Per-launch HBM bytes measured by rocprofv3 counters, if recorded for the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sparse", choices=sorted(W.CONFIGS))
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in DESIGN.md "
+                                   "but not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import nvfp4_compressed_sparse_amd as M
+
+    cfg = W.CONFIGS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} topk={cfg.topk} fmt={cfg.fmt}")
+    t0 = time.time()
+    inp = W.device_inputs(cfg, dev, n_sets=N_SETS)
+    lay = inp["layout"]
+    pool = torch.zeros(lay.num_pages * cfg.page_stride, dtype=torch.uint8, device=dev)
+    quant = M.mla_kv_quant_nvfp4 if cfg.fmt == "nvfp4" else M.mla_kv_quant_fp8
+    quant(inp["lat"], inp["rope"], inp["slots"], pool, cfg.page_stride, lay.num_pages)
+    torch.cuda.synchronize()
+    log(f"[bench] pool filled: {pool.numel() / 1e9:.2f} GB, {inp['slots'].numel()} rows ({time.time() - t0:.1f} s)")
+
+    # the step's own new rows: position L-T+t of every request (or the mixed step's write chunk)
+    if cfg.quant_chunk:
+        w_lat, w_rope, w_slots = inp["chunk_lat"], inp["chunk_rope"], inp["chunk_slots"]
+    else:
+        rows = torch.from_numpy(np.concatenate([inp["row_off"][b] + lay.ctx[b] - cfg.T + np.arange(cfg.T)
+                                                for b in range(cfg.B)]).astype(np.int64)).to(dev)
+        w_lat, w_rope, w_slots = inp["lat"][rows].contiguous(), inp["rope"][rows].contiguous(), inp["slots"][rows]
+
+    # oracle sample (built before the source rows are released)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = prepare_cpu_sample(cfg, inp, args.cpu_sample)
+    del inp["lat"], inp["rope"], inp["slots"]
+    torch.cuda.empty_cache()
+
+    q_sets, idx_sets = inp["q_sets"], inp["idx_sets"]
+    S = args.splits or (M.mla_sparse_decode_splits(cfg.B, cfg.T, cfg.H, cfg.topk) if cfg.topk else
+                        M.mla_dense_decode_splits(cfg.B, cfg.T, cfg.H, int(lay.ctx.max())))
+    if cfg.topk:
+        ws_bytes = M.mla_sparse_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S)
+    else:
+        ws_bytes = M.mla_dense_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, int(lay.ctx.max()), S)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.B, cfg.T, cfg.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    max_ctx = int(lay.ctx.max())
+
+    # valid selected rows per set (algorithmic work)
+    if cfg.topk:
+        lims = np.array([[W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) for t in range(cfg.T)]
+                         for b in range(cfg.B)])
+        lim_d = torch.from_numpy(lims).to(dev)[..., None]
+        valid = [int(((ix >= 0) & (ix <= lim_d)).sum().item()) for ix in idx_sets]
+    else:
+        valid = [int(sum(min(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1, int(lay.ctx[b]))
+                         for b in range(cfg.B) for t in range(cfg.T)))] * N_SETS
+
+    def step(i, ev=None):
+        k = i % N_SETS
+        quant(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        if cfg.topk:
+            M.mla_sparse_decode(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k],
+                                cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
+                                stream=stream)
+        else:
+            M.mla_dense_decode_fp8(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], max_ctx,
+                                   cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
+                                   stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps), splits={S}")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / args.steps
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    dec_avg_us = float(np.mean(dec_us))
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (events), wall {wall / args.steps * 1e6:.2f} "
+        f"us/step; decode call avg {dec_avg_us:.2f} us, p10 {np.percentile(dec_us, 10):.2f}, "
+        f"p90 {np.percentile(dec_us, 90):.2f}")
+
+    nq = cfg.B * cfg.T
+    value = nq / (ms_per_step * 1e-3)
+    vrows = float(np.mean([valid[i % N_SETS] for i in range(args.steps)]))
+    bytes_per, flops_per = algorithmic_work(cfg, vrows)
+    if cfg.H <= 32:
+        ach = bytes_per / (dec_avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops_per / (dec_avg_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_from_profile(cfg.name)
+    roof["kernel"] = "mla_sparse_decode call (decode_kernel + merge_kernel)" if cfg.topk else \
+        "mla_dense_decode_fp8 call (decode_kernel + merge_kernel)"
+    roof["algorithmic_bytes_per_launch"] = int(bytes_per)
+    roof["flops_per_launch"] = flops_per
+    roof["launch_us"] = round(dec_avg_us, 3)
+
+    res = {
+        "metric": "NVFP4 sparse-MLA decode query-tokens/s at B=64, top-2048; % of roofline",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "H": cfg.H, "topk": cfg.topk,
+                   "context": cfg.ctx or list(cfg.ctx_range), "row_bytes": cfg.row_bytes, "page_tokens": 64,
+                   "causal": cfg.causal, "splits": S, "step": ("quantize %d rows + decode" %
+                                                               (cfg.quant_chunk or nq))},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if cpu is not None:
+        res["cpu_baseline"] = run_cpu_baseline(cfg, cpu)
+    print(json.dumps(res), flush=True)
+
+
+def prepare_cpu_sample(cfg, inp, n_sample):
+    """Host copies for the oracle over a bounded sample of the step's query tokens: the selected source
+    rows of the sampled tokens, and the tokens' own new rows."""
+    import torch
+    lay = inp["layout"]
+    nq = cfg.B * cfg.T
+    if n_sample <= 0:
+        n_sample = min(nq, 64)
+    units = np.arange(nq)[:n_sample]
+    idx_all = inp["idx_sets"][0].cpu().numpy() if cfg.topk else None
+    q_all = inp["q_sets"][0].view(torch.int16).cpu().numpy().view(np.uint16)
+    positions = {}
+    for u in units:
+        b, t = divmod(int(u), cfg.T)
+        lim = W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal)
+        if cfg.topk:
+            ids = idx_all[b, t]
+            pos = ids[(ids >= 0) & (ids <= lim)]
+        else:
+            pos = np.arange(lim + 1)
+        positions[b] = np.union1d(positions.get(b, np.zeros(0, np.int64)), pos)
+    src = {}
+    for b, pos in positions.items():
+        rows = torch.from_numpy(inp["row_off"][b] + pos).to("cuda")
+        src[b] = (pos, inp["lat"][rows].view(torch.int16).cpu().numpy().view(np.uint16),
+                  inp["rope"][rows].view(torch.int16).cpu().numpy().view(np.uint16))
+    new_rows = torch.from_numpy(np.array([inp["row_off"][u // cfg.T] + lay.ctx[u // cfg.T] - cfg.T + u % cfg.T
+                                          for u in units], np.int64)).to("cuda")
+    new_lat = inp["lat"][new_rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    new_rope = inp["rope"][new_rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    return dict(units=units, src=src, idx=idx_all, q=q_all, ctx=lay.ctx.copy(), new_lat=new_lat, new_rope=new_rope,
+                max_pages=lay.block_table.shape[1])
+
+
+def run_cpu_baseline(cfg, cpu):
+    """Time the FP64 oracle (as it stands) on this host: quantize-on-write of the sampled tokens' own
+    rows plus the decode of the sampled tokens (one call, threaded over query tokens)."""
+    import oracle
+    nthreads = len(os.sched_getaffinity(0))
+    # setup (untimed): a pool holding the pages of the selected rows, quantized by the oracle
+    bt = np.full((cfg.B, cpu["max_pages"]), -1, np.int32)
+    npg = 1
+    for b, (pos, _, _) in cpu["src"].items():
+        pages = np.unique(pos // 64)
+        bt[b, pages] = np.arange(npg, npg + pages.size)
+        npg += pages.size
+    pool = np.zeros(npg * cfg.page_stride, np.uint8)
+    for b, (pos, lat, rope) in cpu["src"].items():
+        slots = bt[b, pos // 64].astype(np.int64) * 64 + pos % 64
+        oracle.kv_quant(cfg.fmt, lat, rope, slots, pool, cfg.page_stride, npg)
+    n = cpu["units"].size
+    scratch = np.zeros(((n + 63) // 64) * cfg.page_stride, np.uint8)
+    wslots = np.arange(n, dtype=np.int64)
+    times, used = [], 1
+    for rep in range(3):
+        t0 = time.perf_counter()
+        oracle.kv_quant(cfg.fmt, cpu["new_lat"], cpu["new_rope"], wslots, scratch, cfg.page_stride, (n + 63) // 64)
+        if cfg.topk:
+            _, _, used = oracle.sparse_decode(cpu["q"], pool, cfg.page_stride, npg, bt, cpu["ctx"], cpu["idx"],
+                                              cfg.sm_scale, cfg.causal, units=cpu["units"], nthreads=nthreads)
+        else:
+            _, _, used = oracle.dense_decode_fp8(cpu["q"], pool, cfg.page_stride, npg, bt, cpu["ctx"], cfg.sm_scale,
+                                                 cfg.causal, units=cpu["units"], nthreads=nthreads)
+        times.append(time.perf_counter() - t0)
+    tmed = float(np.median(times))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(n / tmed, 3), "unit": "query-tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n} of {cfg.B * cfg.T} query tokens of one step (their row writes + decode), "
+                      f"median of {len(times)} runs of {tmed:.2f} s on {used} threads; {cpu_model}"}
+
+
+if __name__ == "__main__":
+    main()

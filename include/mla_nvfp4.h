@@ -1,0 +1,155 @@
+/*
+ * mla_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 compressed-latent sparse-MLA decode library
+ * (libmla_nvfp4.so).
+ *
+ * The operation (sources: "Prime Inference" launch post, sections "Decode: NVFP4 KV compression" and
+ * "Native NVFP4 sparse MLA decode kernel"; the independent analysis "Prime Inference: serving GLM-5.3
+ * to agents is a KV-cache problem", sections "Four bits per latent value: where 352 comes from" and
+ * "A kernel that reads four bits directly"):
+ *   - every cached token of one layer is one row: a 512-value MLA latent stored as NVFP4 (e2m1
+ *     nibbles, one E4M3 scale per 16 values) and a 64-value rope part stored as E4M3: 352 bytes,
+ *     against 576 bytes for the all-FP8 row;
+ *   - a decode query token attends to at most 2,048 cached positions picked by a sparse top-k
+ *     indexer; unused list entries are -1; the kernel loads only the selected compressed rows and
+ *     unpacks them on chip; scores and outputs accumulate in FP32.
+ *
+ * Row byte layout (NVFP4, 352 bytes):   [0,256)   nibbles, byte i holds element 2i in its low nibble
+ *                                                 and element 2i+1 in its high nibble
+ *                                       [256,288) E4M3 scale of elements 16j..16j+15 at byte 256+j
+ *                                       [288,352) rope, one E4M3 byte per value, no scale
+ * Row byte layout (FP8, 576 bytes):     [0,512) latent E4M3, [512,576) rope E4M3, no scale.
+ * Pool: pages of 64 rows; row `slot` lives at pool + (slot/64)*page_stride_bytes + (slot%64)*row_bytes.
+ * Rounding (the pages fix the format, not the rounding): block scale = E4M3 value nearest to
+ * amax/6, ties to the even code, saturating at 448; element = e2m1 value nearest to |x|/scale, ties
+ * to the even code, saturating at 6 (zero scale -> 0); sign bit copied from the input; rope and
+ * FP8 rows: nearest E4M3, ties to even, saturating at +-448.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are device memory owned by the caller; the library keeps none of
+ *     them after the call returns and allocates nothing.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work on it and
+ *     returns; outputs are valid once the stream reaches that point.  A write into the pool and a
+ *     later decode are ordered only by the caller's stream order.
+ *   - Arguments are checked on the host before anything is enqueued.  On an error status nothing
+ *     is enqueued and no memory is written.  MLA_ERR_HIP reports a failed launch.
+ *   - There is no device-side error reporting: slot entries < 0 or on pages outside
+ *     [0, num_pages) are skipped by the writers; index entries < 0, beyond the query token's limit,
+ *     or on a page-table entry outside [0, num_pages) are ignored by the decoders, as if absent.
+ *   - bf16 arguments are IEEE bfloat16 bit patterns (uint16), non-finite inputs are outside the
+ *     contract.
+ */
+#ifndef MLA_NVFP4_H
+#define MLA_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_QK_DIM 576
+#define MLA_PAGE_TOKENS 64
+#define MLA_NVFP4_ROW_BYTES 352
+#define MLA_FP8_ROW_BYTES 576
+#define MLA_MAX_TOPK 2048
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,        /* a size is out of range (B, T, H, topk, n, num_pages, ...) */
+  MLA_ERR_STRIDE_ALIGN = 3, /* a stride is too small or a pointer / stride is misaligned */
+  MLA_ERR_WORKSPACE = 4,    /* workspace smaller than the matching *_workspace_bytes() */
+  MLA_ERR_DEVICE = 5,       /* the current device is not a gfx950 GPU */
+  MLA_ERR_HIP = 6           /* a HIP launch failed */
+} mla_status;
+
+/* Version of this ABI (MLA_ABI_VERSION). */
+int mla_abi_version(void);
+
+/* Static text for a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * Quantize-on-write, NVFP4 rows (launch post, NVFP4 KV compression; the write API shape follows the
+ * TokenSpeed write-up's MLA KV layout section: separate nope/rope inputs plus a slot-index tensor).
+ *   k_nope        (device) bf16 [n, 512], row r at k_nope + r*nope_stride elements; 16-byte aligned,
+ *                 nope_stride a multiple of 8 and >= 512
+ *   k_rope        (device) bf16 [n, 64], row r at k_rope + r*rope_stride elements; 16-byte aligned,
+ *                 rope_stride a multiple of 8 and >= 64
+ *   slot_mapping  (device) int64 [n]; token r is written to slot slot_mapping[r]; < 0 skips the token
+ *   n             number of tokens, >= 0 (0 enqueues nothing)
+ *   pool          (device) page pool, 16-byte aligned; page_stride_bytes >= 64*352, a multiple of 16
+ *   num_pages     pages in the pool (> 0); slots on pages >= num_pages are skipped
+ * Writes exactly 352 bytes per written token and nothing else.  Two tokens mapped to one slot race.
+ */
+int mla_kv_quant_nvfp4(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                       const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride_bytes,
+                       int64_t num_pages, void* stream);
+
+/* Quantize-on-write, 576-byte FP8 rows (the FP8 cache the pages compare against; analysis, row
+ * table: no per-row scale).  Same arguments and rules as mla_kv_quant_nvfp4, with
+ * page_stride_bytes >= 64*576. */
+int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                     const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride_bytes,
+                     int64_t num_pages, void* stream);
+
+/* Split count the decoders use for this shape when num_splits = 0 (the batch-adaptive choice: the
+ * launch post sizes its cooperating thread-block clusters by batch; here the selected rows of one
+ * query token are split across workgroups instead). */
+int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
+int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context);
+
+/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit). */
+size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
+size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits);
+
+/*
+ * Sparse MLA decode over NVFP4 rows (launch post, native NVFP4 sparse MLA decode kernel).  For every
+ * query token (b, t) and head h, with L = context_lens[b] and limit = causal ? L - T + t : L - 1,
+ * the selection J is the multiset of entries i of indices[b][t][:] with 0 <= i <= limit whose page
+ * entry block_table[b*bt_stride + i/64] is in [0, num_pages).  Each selected row is dequantized to
+ * K[576] (V = K[0..511]); then
+ *     z_i = sm_scale * <q[b][t][h][:], K_i>,   out[b][t][h][:] = sum_i softmax(z)_i V_i,
+ *     lse[b][t][h] = ln sum_i e^{z_i}  (natural log);  empty J gives out = 0, lse = -inf.
+ *   q             (device) bf16 [B, T, H, 576] contiguous, 16-byte aligned (the absorbed query)
+ *   pool          (device) NVFP4 page pool as written by mla_kv_quant_nvfp4; page_stride_bytes as there
+ *   block_table   (device) int32, request b's logical page p at block_table[b*bt_stride + p];
+ *                 at least ceil(context_lens[b]/64) entries per request are read
+ *   context_lens  (device) int32 [B], tokens in each request's cache (the T query tokens included)
+ *   indices       (device) int32 [B, T, topk] logical positions, -1 = unused
+ *   B, T          >= 1;  H in {16, 32, 64, 128};  1 <= topk <= 2048
+ *   causal        0 or 1 (the T query tokens are the last T positions of the request)
+ *   num_splits    0 = the library's choice, else 1..64: the selected rows of each query token are split
+ *                 into this many parts whose results are merged with their log-sum-exp weights
+ *   out           (device) bf16 [B, T, H, 512], 16-byte aligned
+ *   lse           (device) fp32 [B, T, H] or NULL
+ *   workspace     (device) >= mla_sparse_decode_workspace_bytes(...) bytes, 256-byte aligned; may be
+ *                 NULL when that size is 0; contents on entry do not matter
+ */
+int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                      const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                      int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Dense MLA decode over 576-byte FP8 rows: the same definition with J = {0, ..., limit} (every cached
+ * position), the comparison path of the launch post ("FP8 attention").  max_context >= every
+ * context_lens[b] (it sizes the grid); other arguments as for mla_sparse_decode, with the pool
+ * written by mla_kv_quant_fp8 (page_stride_bytes >= 64*576).
+ */
+int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens, int32_t B,
+                         int32_t T, int32_t H, int32_t max_context, float sm_scale, int32_t causal,
+                         int32_t num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_NVFP4_H */

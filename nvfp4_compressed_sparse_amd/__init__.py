@@ -1,0 +1,213 @@
+"""Python binding of libmla_nvfp4 (include/mla_nvfp4.h): NVFP4 compressed-latent sparse-MLA decode on
+MI355X (gfx950).
+
+The functions keep the C names and only marshal arguments: torch tensors supply device pointers,
+strides and the current HIP stream; every step of the computation runs in the library's kernels.
+There is no fallback: if the library cannot be loaded, or a call returns an error status, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB as LIB_PATH
+from .build import build
+
+LATENT_DIM, ROPE_DIM, QK_DIM, PAGE_TOKENS = 512, 64, 576, 64
+NVFP4_ROW_BYTES, FP8_ROW_BYTES, MAX_TOPK = 352, 576, 2048
+
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE_ALIGN", 4: "MLA_ERR_WORKSPACE",
+          5: "MLA_ERR_DEVICE", 6: "MLA_ERR_HIP"}
+
+EXPORTS = [
+    "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
+    "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
+    "mla_sparse_decode", "mla_dense_decode_fp8",
+]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (built in-tree on first use if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "mla_abi_version": (ctypes.c_int, []),
+        "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "mla_kv_quant_nvfp4": (ctypes.c_int, [P, i64, P, i64, P, i64, P, i64, i64, P]),
+        "mla_kv_quant_fp8": (ctypes.c_int, [P, i64, P, i64, P, i64, P, i64, i64, P]),
+        "mla_sparse_decode_splits": (ctypes.c_int, [i32, i32, i32, i32]),
+        "mla_dense_decode_splits": (ctypes.c_int, [i32, i32, i32, i32]),
+        "mla_sparse_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "mla_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "mla_sparse_decode": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
+                                             sz, P]),
+        "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
+                                                sz, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MlaError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# --------------------------------------------------------------------------- quantize-on-write
+
+def _quant(fn_name, k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_pages, stream):
+    import torch
+    _dev(k_nope, torch.bfloat16, "k_nope")
+    _dev(k_rope, torch.bfloat16, "k_rope")
+    _dev(slot_mapping, torch.int64, "slot_mapping")
+    _dev(pool, torch.uint8, "pool")
+    n = slot_mapping.numel()
+    if k_nope.dim() != 2 or k_nope.shape[1] != LATENT_DIM or k_nope.stride(1) != 1 or k_nope.shape[0] != n:
+        raise ValueError("k_nope must be [n, 512] with unit inner stride")
+    if k_rope.dim() != 2 or k_rope.shape[1] != ROPE_DIM or k_rope.stride(1) != 1 or k_rope.shape[0] != n:
+        raise ValueError("k_rope must be [n, 64] with unit inner stride")
+    if not slot_mapping.is_contiguous() or not pool.is_contiguous():
+        raise ValueError("slot_mapping and pool must be contiguous")
+    if pool.numel() < page_stride_bytes * num_pages:
+        raise ValueError("pool smaller than num_pages * page_stride_bytes")
+    st = getattr(lib(), fn_name)(k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+                                 slot_mapping.data_ptr(), n, pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+                                 _stream(stream))
+    _check(fn_name, st)
+
+
+def mla_kv_quant_nvfp4(k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_pages, stream=None):
+    """Write n tokens as 352-byte NVFP4 rows into the page pool (see include/mla_nvfp4.h)."""
+    _quant("mla_kv_quant_nvfp4", k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_pages, stream)
+
+
+def mla_kv_quant_fp8(k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_pages, stream=None):
+    """Write n tokens as 576-byte FP8 rows into the page pool (see include/mla_nvfp4.h)."""
+    _quant("mla_kv_quant_fp8", k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_pages, stream)
+
+
+# --------------------------------------------------------------------------- decode
+
+def mla_sparse_decode_splits(B, T, H, topk):
+    return lib().mla_sparse_decode_splits(B, T, H, topk)
+
+
+def mla_dense_decode_splits(B, T, H, max_context):
+    return lib().mla_dense_decode_splits(B, T, H, max_context)
+
+
+def mla_sparse_decode_workspace_bytes(B, T, H, topk, num_splits=0):
+    return lib().mla_sparse_decode_workspace_bytes(B, T, H, topk, num_splits)
+
+
+def mla_dense_decode_workspace_bytes(B, T, H, max_context, num_splits=0):
+    return lib().mla_dense_decode_workspace_bytes(B, T, H, max_context, num_splits)
+
+
+def _decode_io(q, out, lse, workspace, ws_bytes):
+    import torch
+    B, T, H, _ = q.shape
+    if out is None:
+        out = torch.empty((B, T, H, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+    _dev(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (B, T, H, LATENT_DIM) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, T, H, 512] bf16 tensor")
+    if lse is not None:
+        _dev(lse, torch.float32, "lse")
+        if tuple(lse.shape) != (B, T, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous [B, T, H] fp32 tensor")
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
+    return out, lse, workspace
+
+
+def _common(q, pool, block_table, context_lens):
+    import torch
+    _dev(q, torch.bfloat16, "q")
+    _dev(pool, torch.uint8, "pool")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(context_lens, torch.int32, "context_lens")
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, T, H, 576] bf16 tensor")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table must be [B, pages] with unit inner stride")
+    if context_lens.numel() != q.shape[0] or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+
+
+def mla_sparse_decode(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,
+                      causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Sparse MLA decode over NVFP4 rows; returns (out [B,T,H,512] bf16, lse or None)."""
+    import torch
+    _common(q, pool, block_table, context_lens)
+    _dev(indices, torch.int32, "indices")
+    B, T, H, _ = q.shape
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, T) or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [B, T, topk] int32 tensor")
+    topk = indices.shape[2]
+    ws = lib().mla_sparse_decode_workspace_bytes(B, T, H, topk, int(num_splits))
+    out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
+    st = lib().mla_sparse_decode(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+                                 block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(),
+                                 indices.data_ptr(), B, T, H, topk, float(sm_scale), int(bool(causal)),
+                                 int(num_splits), out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                 None if workspace is None else workspace.data_ptr(),
+                                 0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("mla_sparse_decode", st)
+    return out, lse
+
+
+def mla_dense_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, context_lens, max_context, sm_scale,
+                         causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Dense MLA decode over 576-byte FP8 rows; returns (out [B,T,H,512] bf16, lse or None)."""
+    _common(q, pool, block_table, context_lens)
+    B, T, H, _ = q.shape
+    ws = lib().mla_dense_decode_workspace_bytes(B, T, H, int(max_context), int(num_splits))
+    out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
+    st = lib().mla_dense_decode_fp8(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+                                    block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), B, T, H,
+                                    int(max_context), float(sm_scale), int(bool(causal)), int(num_splits),
+                                    out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                    None if workspace is None else workspace.data_ptr(),
+                                    0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("mla_dense_decode_fp8", st)
+    return out, lse

@@ -1,0 +1,231 @@
+// C ABI of libmla_nvfp4 (declared in include/mla_nvfp4.h): host-side argument checks, the split
+// choice, workspace sizing and launches.  Nothing is enqueued unless every check passes.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "mla_internal.h"
+#include "mla_nvfp4.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_DEVICE;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MLA_OK : MLA_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_heads(int32_t H) { return H == 16 || H == 32 || H == 64 || H == 128; }
+
+int head_groups(int32_t H) { return H == 16 ? 1 : H / 32; }
+
+constexpr int kTargetWorkgroups = 256;  // one resident workgroup per compute unit
+constexpr int kMaxSplits = 64;
+constexpr int kMaxChunk = 2048;  // list entries one workgroup can hold
+constexpr int kTileRows = 64;
+
+int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
+  int64_t s = ceil_div(kTargetWorkgroups, units);
+  int64_t cap = ceil_div(entries, kTileRows);
+  if (s > cap) s = cap;
+  if (s < min_splits) s = min_splits;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) {
+  if (S <= 1) return 0;
+  size_t rows = (size_t)(B * T * H);
+  size_t o_bytes = rows * (size_t)S * 512 * sizeof(float);
+  o_bytes = (o_bytes + 255) & ~(size_t)255;
+  return o_bytes + rows * (size_t)S * sizeof(float);
+}
+
+int check_quant(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride, int64_t num_pages,
+                int row_bytes) {
+  if (n < 0) return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  if (!k_nope || !k_rope || !slot_mapping || !pool) return MLA_ERR_NULL;
+  if (num_pages <= 0) return MLA_ERR_SHAPE;
+  if (nope_stride < 512 || rope_stride < 64 || nope_stride % 8 || rope_stride % 8) return MLA_ERR_STRIDE_ALIGN;
+  if (!aligned(k_nope, 16) || !aligned(k_rope, 16) || !aligned(pool, 16) || !aligned(slot_mapping, 8))
+    return MLA_ERR_STRIDE_ALIGN;
+  if (page_stride < 64LL * row_bytes || page_stride % 16) return MLA_ERR_STRIDE_ALIGN;
+  return MLA_OK;
+}
+
+int run_quant(int fmt, const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+              const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride, int64_t num_pages,
+              void* stream) {
+  int st = check_quant(k_nope, nope_stride, k_rope, rope_stride, slot_mapping, n, pool, page_stride, num_pages,
+                       fmt == 0 ? MLA_NVFP4_ROW_BYTES : MLA_FP8_ROW_BYTES);
+  if (st != MLA_OK || n == 0) return st;
+  if ((st = check_device()) != MLA_OK) return st;
+  mla::QuantArgs a{(const uint16_t*)k_nope, nope_stride, (const uint16_t*)k_rope, rope_stride, slot_mapping, n,
+                   (uint8_t*)pool, page_stride, num_pages};
+  return mla::launch_quant(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int check_decode_common(const void* q, const void* pool, int64_t page_stride, int64_t num_pages,
+                        const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, int32_t B, int32_t T,
+                        int32_t H, float sm_scale, int32_t causal, void* out, int row_bytes) {
+  if (!q || !pool || !block_table || !ctx || !out) return MLA_ERR_NULL;
+  if (B < 1 || T < 1 || !valid_heads(H) || num_pages < 1 || bt_stride < 1) return MLA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
+  if (!(sm_scale == sm_scale)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T * H * 576 > ((int64_t)1 << 40)) return MLA_ERR_SHAPE;
+  if (page_stride < 64LL * row_bytes || page_stride % 16) return MLA_ERR_STRIDE_ALIGN;
+  // row addresses travel as 32-bit multiples of 16 bytes
+  if ((num_pages * page_stride) / 16 > (int64_t)0xFFFFFFFFLL) return MLA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(pool, 16) || !aligned(block_table, 4) || !aligned(ctx, 4))
+    return MLA_ERR_STRIDE_ALIGN;
+  return MLA_OK;
+}
+
+int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, int64_t num_pages,
+               const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, const int32_t* indices, int32_t B,
+               int32_t T, int32_t H, int32_t entries, float sm_scale, int32_t causal, int32_t num_splits, void* out,
+               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int S = num_splits;
+  int chunk = (int)ceil_div(entries, S);
+  if (chunk > kMaxChunk) return MLA_ERR_SHAPE;
+  size_t need = workspace_for(B, T, H, S);
+  if (need > 0) {
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MLA_ERR_STRIDE_ALIGN;
+  }
+  if (lse && !aligned(lse, 4)) return MLA_ERR_STRIDE_ALIGN;
+  int st = check_device();
+  if (st != MLA_OK) return st;
+  mla::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.pool = (const uint8_t*)pool;
+  a.page_stride = page_stride;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.ctx = ctx;
+  a.indices = indices;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.entries = entries;
+  a.chunk = chunk;
+  a.splits = S;
+  a.causal = causal;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  size_t rows = (size_t)B * T * H;
+  size_t o_bytes = ((rows * (size_t)S * 512 * sizeof(float)) + 255) & ~(size_t)255;
+  a.part_o = need ? (float*)workspace : nullptr;
+  a.part_lse = need ? (float*)((char*)workspace + o_bytes) : nullptr;
+  return mla::launch_decode(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size is out of range";
+    case MLA_ERR_STRIDE_ALIGN: return "a stride is too small or a pointer/stride is misaligned";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    case MLA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_kv_quant_nvfp4(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                       const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride_bytes,
+                       int64_t num_pages, void* stream) {
+  return run_quant(0, k_nope, nope_stride, k_rope, rope_stride, slot_mapping, n, pool, page_stride_bytes, num_pages,
+                   stream);
+}
+
+int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                     const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                     void* stream) {
+  return run_quant(1, k_nope, nope_stride, k_rope, rope_stride, slot_mapping, n, pool, page_stride_bytes, num_pages,
+                   stream);
+}
+
+int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk) {
+  if (B < 1 || T < 1 || !valid_heads(H) || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  return auto_splits((int64_t)B * T * head_groups(H), topk, 1);
+}
+
+int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context) {
+  if (B < 1 || T < 1 || !valid_heads(H) || max_context < 1) return 0;
+  return auto_splits((int64_t)B * T * head_groups(H), max_context, ceil_div(max_context, kMaxChunk));
+}
+
+size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
+  int S = num_splits > 0 ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
+  if (S < 1) return 0;
+  return workspace_for(B, T, H, S);
+}
+
+size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits) {
+  int S = num_splits > 0 ? num_splits : mla_dense_decode_splits(B, T, H, max_context);
+  if (S < 1) return 0;
+  return workspace_for(B, T, H, S);
+}
+
+int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                      const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                      int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, B, T, H,
+                               sm_scale, causal, out, MLA_NVFP4_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (!indices) return MLA_ERR_NULL;
+  if (!aligned(indices, 4)) return MLA_ERR_STRIDE_ALIGN;
+  if (topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_SHAPE;
+  int S = num_splits ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
+  return run_decode(0, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
+                    topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens, int32_t B,
+                         int32_t T, int32_t H, int32_t max_context, float sm_scale, int32_t causal, int32_t num_splits,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, B, T, H,
+                               sm_scale, causal, out, MLA_FP8_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (max_context < 1) return MLA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_SHAPE;
+  int S = num_splits ? num_splits : mla_dense_decode_splits(B, T, H, max_context);
+  return run_decode(1, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, nullptr, B, T, H,
+                    max_context, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

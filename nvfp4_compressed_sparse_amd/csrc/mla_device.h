@@ -1,0 +1,151 @@
+// Device-side helpers shared by the gfx950 kernels of libmla_nvfp4: vector types, exact number-format
+// conversions, MFMA wrapper, cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kQK = 576;
+constexpr int kPage = 64;
+constexpr int kNvfp4Row = 352;
+constexpr int kFp8Row = 576;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Upper halves of two fp32 values packed as bf16x2 (lo in bits 0..15).  Exact for values that are
+// representable in bf16, which every dequantized NVFP4 / FP8 product is.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Round-to-nearest-even fp32 -> bf16x2 (hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two e2m1 nibbles of byte `sel` of `src` -> fp32 (low nibble in .x).  The hardware scale operand
+// only contributes its exponent, so it is left at 1.0 and the E4M3 block scale is applied by a
+// separate fp32 multiply (exact: at most 6 significant bits).
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+
+// E4M3FN byte `SEL` of `src` -> fp32 (exact).
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t src) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)src, SEL);
+}
+
+// Two E4M3FN bytes (bytes 2*HI, 2*HI+1 of src) -> bf16x2 (exact at scale 1.0).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t src) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, HI));
+}
+
+// Two E4M3FN bytes (bytes 2*HI, 2*HI+1 of src) -> fp32 pair (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(src, 1.0f, HI);
+}
+
+// Exact value of a non-negative E4M3FN code c (0..126) as fp32, from the format's definition.
+__device__ __forceinline__ float e4m3_code_value(int c) {
+  int e = c >> 3, m = c & 7;
+  float sub = (float)m * 0x1p-9f;
+  float nrm = __uint_as_float((uint32_t)((e + 120) << 23) | ((uint32_t)m << 20));
+  return e == 0 ? sub : nrm;
+}
+
+// Nearest E4M3FN code (0..126) to amax / 6, ties to the even code, saturating at 448.  Binary search
+// over the exact midpoints between neighbouring codes: 6 * (v(k) + v(k+1)) / 2 is exact in fp32.
+__device__ __forceinline__ int e4m3_scale_code_div6(float amax) {
+  int lo = 0, hi = 126;
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    int mid = (lo + hi + 1) >> 1;
+    int k = mid - 1;  // is amax/6 past the midpoint between codes k and k+1?
+    float thr = 3.0f * (e4m3_code_value(k) + e4m3_code_value(k + 1));
+    bool up = (amax > thr) || (amax == thr && ((k + 1) & 1) == 0);
+    if (lo < hi) {
+      if (up) lo = mid;
+      else hi = mid - 1;
+    }
+  }
+  return lo;
+}
+
+// Nearest E4M3FN byte to a finite fp32 value, ties to even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7FFFFFFFu;
+  uint32_t code;
+  if (u >= 0x43E00000u) {  // |x| >= 448
+    code = 0x7E;
+  } else if (u < 0x3C800000u) {  // |x| < 2^-6: multiples of 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
+  } else {
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// e2m1 magnitude code (0..7) of a / s, nearest grid point of {0,.5,1,1.5,2,3,4,6}, ties to the even
+// code, saturating at 6.  Thresholds s * {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} are exact in fp32.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
+  uint32_t c = 0;
+  c += (a > 0.25f * s);
+  c += (a >= 0.75f * s);
+  c += (a > 1.25f * s);
+  c += (a >= 1.75f * s);
+  c += (a > 2.5f * s);
+  c += (a >= 3.5f * s);
+  c += (a > 5.0f * s);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// Workgroup barrier ordering LDS accesses only: global loads still in flight (the next tile's row
+// gather) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Map the hardware workgroup id to a logical id so that logically consecutive workgroups run on the
+// same XCD (workgroups are dealt to the 8 XCDs round-robin; each XCD has its own L2).
+__device__ __forceinline__ int xcd_logical_id(int hw, int n) {
+  const int nx = 8;
+  int q = n / nx, r = n % nx;
+  int x = hw % nx, k = hw / nx;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace mla

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (mla_abi.hip) and the kernels.  Arguments are already
+// validated when these structs are filled.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct QuantArgs {
+  const uint16_t* k_nope;
+  int64_t nope_stride;
+  const uint16_t* k_rope;
+  int64_t rope_stride;
+  const int64_t* slot_mapping;
+  int64_t n;
+  uint8_t* pool;
+  int64_t page_stride;
+  int64_t num_pages;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;          // [B,T,H,576]
+  const uint8_t* pool;
+  int64_t page_stride;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* ctx;         // [B]
+  const int32_t* indices;     // [B,T,topk] (sparse) or nullptr (dense)
+  int B, T, H;
+  int entries;                // topk (sparse) or max_context (dense): length of the position list
+  int chunk;                  // entries per split
+  int splits;                 // S
+  int causal;
+  float scale_log2;           // sm_scale * log2(e)
+  uint16_t* out;              // bf16 [B,T,H,512]
+  float* lse;                 // [B,T,H] or nullptr
+  float* part_o;              // [B*T*H, S, 512] when S > 1
+  float* part_lse;            // [B*T*H, S]
+};
+
+hipError_t launch_quant(int fmt, const QuantArgs& a, hipStream_t stream);
+hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,106 @@
+"""Shared builders for the tests: seeded inputs (workloads), the oracle's results, and the device copies
+the HIP path gets.  Both sides receive the same bf16 inputs; the oracle quantizes its own pool."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads as W
+
+# Tolerances for bf16 attention outputs against the FP64 oracle (see the design notes: the 2e-2
+# absolute bound is applied in units of max(1, |reference|), since bf16 rounding of outputs larger
+# than 8 alone exceeds 2e-2).
+MAX_ERR = 2e-2
+REL_L2 = 1e-2
+LSE_ABS = 1e-3
+
+
+def compare_outputs(gpu_out: np.ndarray, ref_out: np.ndarray, gpu_lse=None, ref_lse=None, what=""):
+    g = gpu_out.astype(np.float64)
+    d = np.abs(g - ref_out)
+    scaled = d / np.maximum(1.0, np.abs(ref_out))
+    nrm = np.linalg.norm(ref_out)
+    rel = np.linalg.norm(g - ref_out) / (nrm if nrm > 0 else 1.0)
+    info = f"{what}: max|d|={d.max():.3e} max scaled={scaled.max():.3e} rel-L2={rel:.3e}"
+    assert scaled.max() <= MAX_ERR, info
+    assert rel <= REL_L2, info
+    if ref_lse is not None:
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(gpu_lse)), what + ": -inf pattern of lse"
+        if fin.any():
+            dl = np.abs(gpu_lse[fin] - ref_lse[fin]).max()
+            assert dl <= LSE_ABS, f"{info} lse max|d|={dl:.3e}"
+    return info
+
+
+class Case:
+    """A complete decode problem on the host: pool source rows, layout, queries, indices."""
+
+    def __init__(self, cfg: W.DecodeConfig, seed_offset: int = 0, ctx=None, indices=None, q=None):
+        rng = np.random.default_rng(cfg.seed + seed_offset)
+        self.cfg = cfg
+        self.lay = W.gen_layout(cfg, rng, ctx=None if ctx is None else np.asarray(ctx, np.int32))
+        lat, rope, slots = [], [], []
+        for b in range(cfg.B):
+            pos = np.arange(int(self.lay.ctx[b]))
+            la, ro = W.gen_latent_rope(rng, pos.size)
+            lat.append(la)
+            rope.append(ro)
+            slots.append(W.slots_for_request(self.lay, b, pos))
+        self.lat = np.concatenate(lat)
+        self.rope = np.concatenate(rope)
+        self.slots = np.concatenate(slots).astype(np.int64)
+        self.q = W.gen_q(rng, cfg.B, cfg.T, cfg.H) if q is None else q
+        if indices is not None:
+            self.idx = indices
+        elif cfg.topk:
+            self.idx = W.gen_indices(rng, self.lay.ctx, cfg.T, cfg.topk, cfg.causal)
+        else:
+            self.idx = None
+        self.rng = rng
+        self._pool = None
+
+    @property
+    def pool_bytes(self):
+        return self.lay.num_pages * self.cfg.page_stride
+
+    def oracle_pool(self):
+        if self._pool is None:
+            pool = np.zeros(self.pool_bytes, np.uint8)
+            oracle.kv_quant(self.cfg.fmt, self.lat, self.rope, self.slots, pool, self.cfg.page_stride,
+                            self.lay.num_pages)
+            self._pool = pool
+        return self._pool
+
+    def oracle_decode(self, idx=None, units=None):
+        pool = self.oracle_pool()
+        c = self.cfg
+        if c.topk:
+            return oracle.sparse_decode(self.q, pool, c.page_stride, self.lay.num_pages, self.lay.block_table,
+                                        self.lay.ctx, self.idx if idx is None else idx, c.sm_scale, c.causal,
+                                        units=units)[:2]
+        return oracle.dense_decode_fp8(self.q, pool, c.page_stride, self.lay.num_pages, self.lay.block_table,
+                                       self.lay.ctx, c.sm_scale, c.causal, units=units)[:2]
+
+    # ---- device side
+    def to_device(self):
+        import torch
+        dev = "cuda"
+        c = self.cfg
+        d = {}
+        d["lat"] = torch.from_numpy(self.lat.view(np.int16)).to(dev).view(torch.bfloat16)
+        d["rope"] = torch.from_numpy(self.rope.view(np.int16)).to(dev).view(torch.bfloat16)
+        d["slots"] = torch.from_numpy(self.slots).to(dev)
+        d["q"] = torch.from_numpy(self.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        d["bt"] = torch.from_numpy(self.lay.block_table).to(dev)
+        d["ctx"] = torch.from_numpy(self.lay.ctx).to(dev)
+        if self.idx is not None:
+            d["idx"] = torch.from_numpy(self.idx).to(dev)
+        d["pool"] = torch.zeros(self.pool_bytes, dtype=torch.uint8, device=dev)
+        return d
+
+
+def bf16_to_np(t) -> np.ndarray:
+    """bf16 device tensor -> float64 numpy array (exact)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)

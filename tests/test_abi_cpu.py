@@ -1,0 +1,136 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol include/mla_nvfp4.h declares,
+and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_compressed_sparse_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "mla_nvfp4.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 10
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_version_and_status_strings():
+    L = M.lib()
+    assert L.mla_abi_version() == 1
+    for s in range(7):
+        assert L.mla_status_string(s)
+    assert L.mla_status_string(0) == b"ok"
+
+
+FAKE = 1 << 20  # a 16/256-byte aligned fake device address; never dereferenced (checks fail first)
+
+
+def _sparse(**kw):
+    a = dict(q=FAKE, pool=FAKE, ps=64 * 352, npg=10, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, B=2, T=1, H=16, k=256,
+             sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return M.lib().mla_sparse_decode(a["q"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"], a["idx"],
+                                     a["B"], a["T"], a["H"], a["k"], a["sc"], a["causal"], a["S"], a["out"],
+                                     a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sparse_decode_argument_errors():
+    assert _sparse(q=None) == 1
+    assert _sparse(idx=None) == 1
+    assert _sparse(out=None) == 1
+    assert _sparse(B=0) == 2
+    assert _sparse(T=0) == 2
+    assert _sparse(H=48) == 2
+    assert _sparse(k=0) == 2
+    assert _sparse(k=2049) == 2
+    assert _sparse(causal=2) == 2
+    assert _sparse(S=65) == 2
+    assert _sparse(npg=0) == 2
+    assert _sparse(ps=64 * 352 - 16) == 3
+    assert _sparse(ps=64 * 352 + 8) == 3
+    assert _sparse(q=FAKE + 8) == 3
+    assert _sparse(out=FAKE + 2) == 3
+    assert _sparse(sc=float("nan")) == 2
+    # split path needs a workspace of the advertised size
+    need = M.lib().mla_sparse_decode_workspace_bytes(2, 1, 16, 256, 4)
+    assert need > 0
+    assert _sparse(S=4) == 1
+    assert _sparse(S=4, ws=FAKE, wsb=need - 1) == 4
+    assert _sparse(S=4, ws=FAKE + 16, wsb=need) == 3
+    # valid arguments reach the device check: no gfx950 device here
+    import torch
+    if not torch.cuda.is_available():
+        assert _sparse(S=4, ws=FAKE, wsb=need) == 5
+        assert _sparse(S=1) == 5
+
+
+def _dense(**kw):
+    a = dict(q=FAKE, pool=FAKE, ps=64 * 576, npg=10, bt=FAKE, bts=4, ctx=FAKE, B=2, T=1, H=128, L=8192,
+             sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return M.lib().mla_dense_decode_fp8(a["q"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"], a["B"],
+                                        a["T"], a["H"], a["L"], a["sc"], a["causal"], a["S"], a["out"], a["lse"],
+                                        a["ws"], a["wsb"], a["stream"])
+
+
+def test_dense_decode_argument_errors():
+    assert _dense(pool=None) == 1
+    assert _dense(L=0) == 2
+    assert _dense(H=8) == 2
+    assert _dense(ps=64 * 352) == 3  # an NVFP4-sized page is too small for 576-byte rows
+    assert _dense(S=2) == 2  # 8192 positions in 2 splits exceeds the 2048 entries one workgroup holds
+
+
+def _quant(fn="mla_kv_quant_nvfp4", **kw):
+    a = dict(kn=FAKE, ns=512, kr=FAKE, rs=64, sl=FAKE, n=4, pool=FAKE, ps=64 * 352, npg=4, stream=None)
+    a.update(kw)
+    return getattr(M.lib(), fn)(a["kn"], a["ns"], a["kr"], a["rs"], a["sl"], a["n"], a["pool"], a["ps"], a["npg"],
+                                a["stream"])
+
+
+def test_quant_argument_errors():
+    assert _quant(n=0, kn=None) == 0  # nothing to do
+    assert _quant(n=-1) == 2
+    assert _quant(kn=None) == 1
+    assert _quant(sl=None) == 1
+    assert _quant(ns=511) == 3
+    assert _quant(rs=60) == 3
+    assert _quant(ns=516) == 3
+    assert _quant(kn=FAKE + 2) == 3
+    assert _quant(npg=0) == 2
+    assert _quant("mla_kv_quant_fp8", ps=64 * 352) == 3
+
+
+def test_split_choice_and_workspace_sizes():
+    L = M.lib()
+    # one resident workgroup per compute unit: 64 query tokens x 1 head group -> 4 splits
+    assert L.mla_sparse_decode_splits(64, 1, 32, 2048) == 4
+    assert L.mla_sparse_decode_splits(128, 4, 32, 2048) == 1
+    assert L.mla_sparse_decode_splits(256, 1, 128, 2048) == 1
+    assert L.mla_sparse_decode_splits(2, 1, 16, 256) == 4  # capped at one 64-row tile per split
+    assert L.mla_dense_decode_splits(16, 1, 128, 8192) == 4
+    assert L.mla_dense_decode_splits(4, 1, 128, 8192) == 16
+    assert L.mla_sparse_decode_splits(0, 1, 32, 2048) == 0
+    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 1) == 0
+    rows = 64 * 32
+    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 4) == rows * 4 * 512 * 4 + rows * 4 * 4
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        M.mla_kv_quant_nvfp4(torch.zeros(1, 512, dtype=torch.bfloat16), torch.zeros(1, 64, dtype=torch.bfloat16),
+                             torch.zeros(1, dtype=torch.int64), torch.zeros(22528, dtype=torch.uint8), 22528, 1)

@@ -1,0 +1,370 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle on the same seeded inputs.
+
+Quantized bytes must match bit for bit; attention outputs must meet the tolerances in cases.py."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from cases import Case, bf16_to_np, compare_outputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import nvfp4_compressed_sparse_amd as M  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name="t", B=2, T=1, H=16, topk=256, L=4096, fmt="nvfp4", causal=False, seed=7):
+    return W.DecodeConfig(name, B=B, T=T, H=H, topk=topk, fmt=fmt, ctx=L, causal=causal, seed=seed)
+
+
+def gpu_pool(case, d):
+    c = case.cfg
+    fn = M.mla_kv_quant_nvfp4 if c.fmt == "nvfp4" else M.mla_kv_quant_fp8
+    fn(d["lat"], d["rope"], d["slots"], d["pool"], c.page_stride, case.lay.num_pages)
+    torch.cuda.synchronize()
+    return d["pool"]
+
+
+def gpu_decode(case, d, num_splits=0, idx=None, q=None):
+    c = case.cfg
+    lse = torch.empty((c.B, c.T, c.H), dtype=torch.float32, device="cuda")
+    qq = d["q"] if q is None else q
+    if c.topk:
+        out, _ = M.mla_sparse_decode(qq, d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"],
+                                     d["idx"] if idx is None else idx, c.sm_scale, causal=c.causal,
+                                     num_splits=num_splits, lse=lse)
+    else:
+        out, _ = M.mla_dense_decode_fp8(qq, d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"],
+                                        int(case.lay.ctx.max()), c.sm_scale, causal=c.causal,
+                                        num_splits=num_splits, lse=lse)
+    torch.cuda.synchronize()
+    return bf16_to_np(out).reshape(c.B * c.T, c.H, 512), lse.cpu().numpy().astype(np.float64).reshape(c.B * c.T, c.H)
+
+
+# --------------------------------------------------------------------------- quantize-on-write: bit exact
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_quant_pool_bit_exact(fmt):
+    case = Case(small(fmt=fmt, topk=256 if fmt == "nvfp4" else 0, L=3000, seed=11))
+    say(f"quant pool {fmt}: {case.slots.size} rows")
+    d = case.to_device()
+    g = gpu_pool(case, d).cpu().numpy()
+    ref = case.oracle_pool()
+    bad = np.nonzero(g != ref)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
+def _adversarial_rows():
+    """Rows that cover every finite bf16 value as latent and rope entries, every scale tie, zero /
+    negative-zero / subnormal-scale / saturating blocks."""
+    fin = np.array([b for b in range(65536) if ((b >> 7) & 0xFF) != 0xFF], dtype=np.uint16)
+    rows = []
+    # every finite bf16 value inside blocks of its own neighbourhood (sorted by magnitude), and shuffled
+    srt = fin[np.argsort(np.abs(W.bf16_to_f32(fin)), kind="stable")]
+    n = (srt.size // 512) * 512
+    rows.append(srt[:n].reshape(-1, 512))
+    rng = np.random.default_rng(3)
+    rows.append(rng.permutation(fin)[:n].reshape(-1, 512))
+    # scale ties: amax exactly 6 x the midpoint of two neighbouring E4M3 values (plus neighbours)
+    ties = []
+    for c in range(0x7E):
+        m6 = 3.0 * (oracle.e4m3_value(c) + oracle.e4m3_value(c + 1))
+        b = W.bf16_bits(np.array([m6], np.float32))[0]
+        if W.bf16_to_f32(np.array([b]))[0] == m6:
+            ties.append(b)
+    ties = np.array(ties, np.uint16)
+    blk = rng.choice(fin[(fin >> 15) == 0][:20000], size=(ties.size, 16))  # small magnitudes
+    blk[:, 0] = ties
+    blk[:, 5] = ties | 0x8000
+    pad = (-blk.shape[0]) % 32
+    blk = np.concatenate([blk, np.zeros((pad, 16), np.uint16)])
+    rows.append(blk.reshape(-1, 512))
+    special = np.zeros((4, 512), np.uint16)
+    special[0, 16:32] = 0x8000  # negative zeros
+    special[1] = W.bf16_bits(rng.standard_normal(512).astype(np.float32) * 1e-3)  # subnormal scales
+    special[2] = W.bf16_bits(rng.standard_normal(512).astype(np.float32) * 1e4)  # saturating blocks
+    special[3] = W.bf16_bits(np.where(rng.random(512) < 0.5, 1e30, -1e-30).astype(np.float32))
+    rows.append(special)
+    lat = np.concatenate(rows)
+    rope_src = np.concatenate([fin, fin[: (-fin.size) % 64]])
+    rope = np.resize(rng.permutation(rope_src), (lat.shape[0], 64)).astype(np.uint16)
+    return lat, rope
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_quant_adversarial_rows_bit_exact(fmt):
+    lat, rope = _adversarial_rows()
+    n = lat.shape[0]
+    rb = 352 if fmt == "nvfp4" else 576
+    page_stride = 64 * rb + 48  # a padded page stride
+    num_pages = (n + 63) // 64 + 2
+    rng = np.random.default_rng(9)
+    slots = rng.permutation(num_pages * 64)[:n].astype(np.int64)
+    slots[::97] = -1  # skipped tokens
+    slots[5] = num_pages * 64 + 3  # on a page outside the pool: skipped
+    say(f"adversarial quant {fmt}: {n} rows")
+    ref = np.zeros(num_pages * page_stride, np.uint8)
+    oracle.kv_quant(fmt, lat, rope, slots, ref, page_stride, num_pages)
+    pool = torch.zeros(num_pages * page_stride, dtype=torch.uint8, device="cuda")
+    kn = torch.from_numpy(lat.view(np.int16)).cuda().view(torch.bfloat16)
+    kr = torch.from_numpy(rope.view(np.int16)).cuda().view(torch.bfloat16)
+    fn = M.mla_kv_quant_nvfp4 if fmt == "nvfp4" else M.mla_kv_quant_fp8
+    fn(kn, kr, torch.from_numpy(slots).cuda(), pool, page_stride, num_pages)
+    g = pool.cpu().numpy()
+    bad = np.nonzero(g != ref)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
+def test_quant_strided_inputs_from_one_kv_tensor():
+    # nope and rope as views of one [n, 576] tensor (stride 576), written through a pool of 2 layers
+    rng = np.random.default_rng(21)
+    lat, rope = W.gen_latent_rope(rng, 700)
+    kv = np.concatenate([lat, rope], axis=1)
+    kvd = torch.from_numpy(kv.view(np.int16)).cuda().view(torch.bfloat16)
+    layers, pages = 2, 12
+    page_stride = layers * 64 * 352  # block-major: pages hold both layers' rows
+    pool = torch.zeros(pages * page_stride, dtype=torch.uint8, device="cuda")
+    slots = rng.permutation(pages * 64)[:700].astype(np.int64)
+    layer1 = pool[64 * 352:]  # layer 1 rows start 64*352 bytes into each page
+    M.mla_kv_quant_nvfp4(kvd[:, :512], kvd[:, 512:], torch.from_numpy(slots).cuda(), layer1, page_stride, pages - 1)
+    ref = np.zeros(pages * page_stride, np.uint8)
+    oracle.kv_quant("nvfp4", lat, rope, slots, ref[64 * 352:], page_stride, pages - 1)
+    assert np.array_equal(pool.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------------------- sparse decode
+def test_sparse_decode_tiny_config():
+    case = Case(W.CONFIGS["tiny"])
+    say("tiny config decode")
+    d = case.to_device()
+    gpu_pool(case, d)
+    assert np.array_equal(d["pool"].cpu().numpy(), case.oracle_pool())
+    out, lse = gpu_decode(case, d)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, "tiny"))
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 64])
+def test_sparse_decode_split_counts(S):
+    case = Case(small(H=32, topk=300, L=5000, seed=13))  # 300 = 4 full tiles + a ragged 44
+    say(f"split count {S}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d, num_splits=S)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"S={S}"))
+
+
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+@pytest.mark.parametrize("topk", [1, 77, 2048])
+def test_sparse_decode_heads_and_topk(H, topk):
+    case = Case(small(B=3, H=H, topk=topk, L=9000, seed=100 + H + topk))
+    say(f"H={H} topk={topk}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"H={H} topk={topk}"))
+
+
+def test_sparse_decode_padding_and_invalid_entries():
+    cfg = small(B=4, H=32, topk=512, L=2000, seed=17)
+    rng = np.random.default_rng(5)
+    case = Case(cfg)
+    idx = case.idx.copy()
+    # -1 runs, entries past the context, far out of range, negative garbage
+    idx[0, 0, :200] = -1
+    idx[1, 0, rng.choice(512, 100, replace=False)] = -1
+    idx[2, 0, :10] = 2000
+    idx[2, 0, 10:20] = 10 ** 8
+    idx[2, 0, 20:30] = -5
+    idx[3, 0, :] = -1  # empty selection
+    case.idx = idx
+    # a page-table entry outside the pool drops the positions on that page
+    bt = case.lay.block_table
+    bt[1, 3] = case.lay.num_pages + 5
+    say("padding / invalid entries")
+    d = case.to_device()
+    gpu_pool(case, d)
+    for S in (1, 4):
+        out, lse = gpu_decode(case, d, num_splits=S)
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(out, ro, lse, rl, f"invalid entries S={S}"))
+        assert not out[3].any() and np.all(lse[3] == -np.inf)
+
+
+def test_sparse_decode_causal_speculative_verify():
+    cfg = small(B=3, T=4, H=32, topk=256, L=3000, causal=True, seed=19)
+    case = Case(cfg, ctx=[3000, 700, 260])
+    # some entries beyond each token's own limit (inside the context) must be ignored
+    for b in range(3):
+        L = int(case.lay.ctx[b])
+        case.idx[b, 0, :3] = [L - 1, L - 2, L - 3]
+    say("causal T=4")
+    d = case.to_device()
+    gpu_pool(case, d)
+    for S in (0, 1, 2):
+        out, lse = gpu_decode(case, d, num_splits=S)
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(out, ro, lse, rl, f"causal S={S}"))
+
+
+def test_single_index_returns_that_row_exactly():
+    cfg = small(B=2, H=32, topk=64, L=1000, seed=23)
+    case = Case(cfg)
+    idx = np.full_like(case.idx, -1)
+    idx[:, :, 17] = case.idx[:, :, 0]
+    case.idx = idx
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d, num_splits=1)
+    ro, rl = case.oracle_decode()
+    # P = 1: the output is the dequantized V row itself, which is exact in bf16
+    assert np.array_equal(out, ro)
+    assert np.abs(lse - rl).max() <= 1e-3
+
+
+def test_zero_query_gives_mean_of_v():
+    cfg = small(B=2, H=16, topk=200, L=1500, seed=29)
+    case = Case(cfg)
+    case.q[:] = 0
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d, num_splits=1)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, "q=0"))
+    # all heads see the same uniform weights
+    assert np.array_equal(out[:, 0:1, :].repeat(16, 1), out)
+
+
+def test_permuted_index_list_gives_same_result():
+    cfg = small(B=2, H=32, topk=512, L=4000, seed=31)
+    case = Case(cfg)
+    d = case.to_device()
+    gpu_pool(case, d)
+    out0, lse0 = gpu_decode(case, d, num_splits=1)
+    perm = torch.from_numpy(case.idx[:, :, np.random.default_rng(1).permutation(512)].copy()).cuda()
+    out1, lse1 = gpu_decode(case, d, num_splits=1, idx=perm)
+    ro, rl = case.oracle_decode()
+    compare_outputs(out1, ro, lse1, rl, "permuted")
+    compare_outputs(out0, ro, lse0, rl, "original")
+
+
+# --------------------------------------------------------------------------- dense FP8 decode
+@pytest.mark.parametrize("T,causal,S", [(1, False, 0), (1, False, 1), (2, True, 0), (1, False, 7)])
+def test_dense_fp8_decode(T, causal, S):
+    cfg = small(B=2, T=T, H=128, topk=0, fmt="fp8", L=1100, causal=causal, seed=37)
+    case = Case(cfg, ctx=[1100, 333])
+    say(f"dense fp8 T={T} causal={causal} S={S}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    assert np.array_equal(d["pool"].cpu().numpy(), case.oracle_pool())
+    out, lse = gpu_decode(case, d, num_splits=S)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"dense T={T} S={S}"))
+
+
+# --------------------------------------------------------------------------- full-size configs, sampled
+def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
+    """Oracle results for sampled query tokens of a full-size device case: the selected source rows are
+    copied to the host and quantized by the oracle into a small pool of their own."""
+    lay = inp["layout"]
+    outs, lses, pools_ok = [], [], True
+    idx_all = idx_d.cpu().numpy() if idx_d is not None else None
+    q_all = q_d.view(torch.int16).cpu().numpy().view(np.uint16)
+    for qt in qtoks:
+        b, t = divmod(int(qt), cfg.T)
+        L = int(lay.ctx[b])
+        lim = W.position_limit(L, cfg.T, t, cfg.causal)
+        if idx_all is not None:
+            ids = idx_all[b, t]
+            pos = np.unique(ids[(ids >= 0) & (ids <= lim)])
+        else:
+            pos = np.arange(lim + 1)
+        pages = np.unique(pos // 64)
+        mini_bt = np.full((1, lay.block_table.shape[1]), -1, np.int32)
+        mini_bt[0, pages] = np.arange(1, pages.size + 1)
+        rows = torch.from_numpy(inp["row_off"][b] + pos).cuda()
+        lat = inp["lat"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        rope = inp["rope"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        npg = pages.size + 1
+        pool = np.zeros(npg * cfg.page_stride, np.uint8)
+        slots = (mini_bt[0, pos // 64].astype(np.int64) * 64 + pos % 64)
+        oracle.kv_quant(cfg.fmt, lat, rope, slots, pool, cfg.page_stride, npg)
+        ctx = np.array([L], np.int32)
+        q1 = q_all[b:b + 1]
+        if idx_all is not None:
+            o, l, _ = oracle.sparse_decode(q1, pool, cfg.page_stride, npg, mini_bt, ctx, idx_all[b:b + 1],
+                                           cfg.sm_scale, cfg.causal, units=[t])
+        else:
+            o, l, _ = oracle.dense_decode_fp8(q1, pool, cfg.page_stride, npg, mini_bt, ctx, cfg.sm_scale, cfg.causal,
+                                              units=[t])
+        outs.append(o[0])
+        lses.append(l[0])
+        # the device pool holds the same bytes for these rows
+        gslots = lay.block_table[b, pos // 64].astype(np.int64) * 64 + pos % 64
+        offs = (gslots // 64) * cfg.page_stride + (gslots % 64) * cfg.row_bytes
+        rb = cfg.row_bytes
+        gidx = torch.from_numpy((offs[:, None] + np.arange(rb)[None, :]).reshape(-1)).cuda()
+        grows = inp["pool"][gidx].cpu().numpy().reshape(-1, rb)
+        oidx = (slots // 64) * cfg.page_stride + (slots % 64) * rb
+        orows = pool[(oidx[:, None] + np.arange(rb)[None, :]).reshape(-1)].reshape(-1, rb)
+        pools_ok &= np.array_equal(grows, orows)
+    return np.stack(outs), np.stack(lses), pools_ok
+
+
+@pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b16"])
+def test_full_size_config_sampled(name):
+    cfg = W.CONFIGS[name]
+    say(f"full-size {name}: generating inputs")
+    inp = W.device_inputs(cfg, "cuda", n_sets=1)
+    lay = inp["layout"]
+    pool = torch.zeros(lay.num_pages * cfg.page_stride, dtype=torch.uint8, device="cuda")
+    inp["pool"] = pool
+    fn = M.mla_kv_quant_nvfp4 if cfg.fmt == "nvfp4" else M.mla_kv_quant_fp8
+    fn(inp["lat"], inp["rope"], inp["slots"], pool, cfg.page_stride, lay.num_pages)
+    if cfg.quant_chunk:
+        fn(inp["chunk_lat"], inp["chunk_rope"], inp["chunk_slots"], pool, cfg.page_stride, lay.num_pages)
+    q = inp["q_sets"][0]
+    lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    say(f"full-size {name}: decode")
+    if cfg.topk:
+        idx = inp["idx_sets"][0]
+        out, _ = M.mla_sparse_decode(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx,
+                                     cfg.sm_scale, causal=cfg.causal, lse=lse)
+    else:
+        idx = None
+        out, _ = M.mla_dense_decode_fp8(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"],
+                                        int(lay.ctx.max()), cfg.sm_scale, causal=cfg.causal, lse=lse)
+    torch.cuda.synchronize()
+    nq = cfg.B * cfg.T
+    qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed).choice(nq, 6, replace=False))))
+    say(f"full-size {name}: oracle on query tokens {qtoks}")
+    ro, rl, pools_ok = _sampled_oracle(cfg, inp, qtoks, idx, q)
+    assert pools_ok, "pool rows differ from the oracle's quantization"
+    g = bf16_to_np(out).reshape(nq, cfg.H, 512)[qtoks]
+    gl = lse.cpu().numpy().astype(np.float64).reshape(nq, cfg.H)[qtoks]
+    say(compare_outputs(g, ro, gl, rl, f"full-size {name}"))
+    # the write chunk of the mixed step: bit exact on every row
+    if cfg.quant_chunk:
+        cl = inp["chunk_lat"].view(torch.int16).cpu().numpy().view(np.uint16)
+        cr = inp["chunk_rope"].view(torch.int16).cpu().numpy().view(np.uint16)
+        cs = inp["chunk_slots"].cpu().numpy()
+        rb = cfg.row_bytes
+        offs = (cs // 64) * cfg.page_stride + (cs % 64) * rb
+        gidx = torch.from_numpy((offs[:, None] + np.arange(rb)[None, :]).reshape(-1)).cuda()
+        grows = pool[gidx].cpu().numpy().reshape(-1, rb)
+        for r in range(0, cs.size, 37):
+            assert np.array_equal(grows[r], oracle.quant_row_nvfp4(cl[r], cr[r]))
+    del inp, pool
+    torch.cuda.empty_cache()

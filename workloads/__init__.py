@@ -200,3 +200,45 @@ def torch_indices(gen, ctx: np.ndarray, T: int, topk: int, causal: bool, device)
             i = torch.cat([i, torch.full((e - s, topk - k), -1, dtype=torch.int32, device=device)], dim=1)
         flat_out[s:e] = i
     return out
+
+
+# --------------------------------------------------------------------------- full-size device inputs
+
+def device_inputs(cfg: DecodeConfig, device="cuda", n_sets: int = 1, row_chunk: int = 1 << 20):
+    """Every input of one step of `cfg`, generated on the device from the config's seed.
+
+    Returns a dict: layout (PoolLayout, host), row_off (host int64 [B+1]: request b's source rows are
+    lat[row_off[b]:row_off[b+1]], position order), lat / rope (bf16 source rows of every cached
+    position), slots (int64 slot of every source row), bt / ctx (device int32), q_sets / idx_sets
+    (n_sets independent query and index sets), and for a config with a write chunk, chunk_lat /
+    chunk_rope / chunk_slots.
+    """
+    import torch
+    rng = np.random.default_rng(cfg.seed)
+    lay = gen_layout(cfg, rng)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed)
+    ctx = lay.ctx.astype(np.int64)
+    row_off = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int64)
+    total = int(row_off[-1])
+    lat = torch.empty((total, LATENT), dtype=torch.bfloat16, device=device)
+    rope = torch.empty((total, ROPE), dtype=torch.bfloat16, device=device)
+    for s in range(0, total, row_chunk):
+        e = min(total, s + row_chunk)
+        lat[s:e] = torch_bf16_normal(gen, (e - s, LATENT), device, scale_rows=True, outliers=True)
+        rope[s:e] = torch_bf16_normal(gen, (e - s, ROPE), device)
+    bt = torch.from_numpy(lay.block_table).to(device)
+    slots = torch.empty(total, dtype=torch.int64, device=device)
+    for b in range(cfg.B):
+        pos = torch.arange(int(ctx[b]), device=device)
+        slots[row_off[b]:row_off[b + 1]] = bt[b][pos >> 6].long() * PAGE + (pos & (PAGE - 1))
+    out = dict(layout=lay, row_off=row_off, lat=lat, rope=rope, slots=slots, bt=bt,
+               ctx=torch.from_numpy(lay.ctx).to(device))
+    out["q_sets"] = [torch_bf16_normal(gen, (cfg.B, cfg.T, cfg.H, QK), device) for _ in range(n_sets)]
+    out["idx_sets"] = ([torch_indices(gen, lay.ctx, cfg.T, cfg.topk, cfg.causal, device) for _ in range(n_sets)]
+                       if cfg.topk else [])
+    if cfg.quant_chunk:
+        out["chunk_lat"] = torch_bf16_normal(gen, (cfg.quant_chunk, LATENT), device, scale_rows=True, outliers=True)
+        out["chunk_rope"] = torch_bf16_normal(gen, (cfg.quant_chunk, ROPE), device)
+        out["chunk_slots"] = torch.from_numpy(gen_chunk_slots(lay, rng, cfg.quant_chunk)).to(device)
+    return out
