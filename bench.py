@@ -190,8 +190,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_from_profile(cfg.name)
-    roof["kernel"] = "mla_sparse_decode call (decode_kernel + merge_kernel)" if cfg.topk else \
-        "mla_dense_decode_fp8 call (decode_kernel + merge_kernel)"
+    roof["kernel"] = "mla_sparse_decode call (decode_kernel + merge_kernel when split)" if cfg.topk else \
+        "mla_dense_decode_fp8 call (decode_kernel + merge_kernel when split)"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)

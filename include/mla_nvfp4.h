@@ -103,7 +103,10 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
 int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context);
 
-/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit). */
+/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): the fp32 partial
+ * outputs and log-sum-exps of the splits, merged by a second small launch on the same stream (the
+ * pages merge a cluster's partial results without one).  Contents on entry do not matter; two calls
+ * that can run concurrently must not share a workspace. */
 size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits);
 

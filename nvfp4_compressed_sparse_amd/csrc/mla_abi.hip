@@ -50,13 +50,24 @@ int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
   return (int)s;
 }
 
-size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) {
-  if (S <= 1) return 0;
-  size_t rows = (size_t)(B * T * H);
-  size_t o_bytes = rows * (size_t)S * 512 * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  return o_bytes + rows * (size_t)S * sizeof(float);
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout when S > 1: [partial outputs: B*T*H*S*512 fp32][partial lse: B*T*H*S fp32], each
+// region 256-byte aligned.
+struct WsLayout {
+  size_t o_off, lse_off, total;
+};
+
+WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
+  WsLayout l{0, 0, 0};
+  if (S <= 1) return l;
+  const size_t rows = (size_t)(B * T * H);
+  l.lse_off = round256(rows * (size_t)S * 512 * sizeof(float));
+  l.total = l.lse_off + round256(rows * (size_t)S * sizeof(float));
+  return l;
 }
+
+size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) { return workspace_layout(B, T, H, S).total; }
 
 int check_quant(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
                 const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride, int64_t num_pages,
@@ -135,10 +146,9 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.out = (uint16_t*)out;
   a.lse = lse;
-  size_t rows = (size_t)B * T * H;
-  size_t o_bytes = ((rows * (size_t)S * 512 * sizeof(float)) + 255) & ~(size_t)255;
-  a.part_o = need ? (float*)workspace : nullptr;
-  a.part_lse = need ? (float*)((char*)workspace + o_bytes) : nullptr;
+  const WsLayout wl = workspace_layout(B, T, H, S);
+  a.part_o = need ? (float*)((char*)workspace + wl.o_off) : nullptr;
+  a.part_lse = need ? (float*)((char*)workspace + wl.lse_off) : nullptr;
   return mla::launch_decode(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

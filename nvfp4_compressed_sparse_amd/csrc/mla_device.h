@@ -20,6 +20,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -41,6 +43,20 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 template <int SEL>
 __device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t src) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+
+// Two e2m1 nibbles of byte `SEL` of `src` -> fp16x2 (low nibble in .x), exact.  As above the hardware
+// scale is left at 1.0; the block scale is applied with a packed fp16 multiply, which is exact too:
+// e2m1 * E4M3 needs at most 6 significant bits and lies in [2^-10, 2688], inside fp16's normal range.
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4x2_to_f16(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, 1.0f, SEL);
+}
+
+// Two E4M3FN bytes (bytes 2*HI, 2*HI+1 of src) -> fp16x2 (exact: every E4M3 value is an fp16 normal).
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, HI);
 }
 
 // E4M3FN byte `SEL` of `src` -> fp32 (exact).
@@ -122,6 +138,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+             __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(f16x8, v);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(bf16x8, v);
@@ -131,13 +157,14 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
-// Workgroup barrier ordering LDS accesses only: global loads still in flight (the next tile's row
-// gather) are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// Workgroup barrier ordering LDS accesses only: this wave's LDS operations complete (lgkmcnt(0)),
+// then s_barrier.  Vector-memory loads still in flight (the next tiles' row gathers into other LDS
+// slots) are not waited for; the "memory" clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until every vector memory load of this wave has landed (vmcnt(0)).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Map the hardware workgroup id to a logical id so that logically consecutive workgroups run on the
 // same XCD (workgroups are dealt to the 8 XCDs round-robin; each XCD has its own L2).
