@@ -207,7 +207,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "H": cfg.H, "topk": cfg.topk,
                    "context": cfg.ctx or list(cfg.ctx_range), "row_bytes": cfg.row_bytes, "page_tokens": 64,

@@ -2,8 +2,8 @@
  * mla_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 compressed-latent sparse-MLA decode library
  * (libmla_nvfp4.so).
  *
- * The operation (sources: "Prime Inference" launch post, sections "Decode: NVFP4 KV compression" and
- * "Native NVFP4 sparse MLA decode kernel"; the independent analysis "Prime Inference: serving GLM-5.3
+ * The operation (sources: "Prime Inference" launch post, sections "为低延迟解码腾出空间" (making room for
+ * low-latency decode) and "原生 NVFP4 稀疏 MLA 解码内核" (native NVFP4 sparse MLA decode kernel); the independent analysis "Prime Inference: serving GLM-5.3
  * to agents is a KV-cache problem", sections "Four bits per latent value: where 352 comes from" and
  * "A kernel that reads four bits directly"):
  *   - every cached token of one layer is one row: a 512-value MLA latent stored as NVFP4 (e2m1
@@ -74,7 +74,7 @@ int mla_abi_version(void);
 const char* mla_status_string(int status);
 
 /*
- * Quantize-on-write, NVFP4 rows (launch post, NVFP4 KV compression; the write API shape follows the
+ * Quantize-on-write, NVFP4 rows (launch post, making room for low-latency decode; the write API shape follows the
  * TokenSpeed write-up's MLA KV layout section: separate nope/rope inputs plus a slot-index tensor).
  *   k_nope        (device) bf16 [n, 512], row r at k_nope + r*nope_stride elements; 16-byte aligned,
  *                 nope_stride a multiple of 8 and >= 512

@@ -1,6 +1,6 @@
 // Quantize-on-write kernels: bf16 latent[512] + rope[64] per token -> one cache row in a paged pool.
 //
-// Row formats ("Prime Inference" launch post, section on NVFP4 KV compression; the analysis page's
+// Row formats ("Prime Inference" launch post, section "为低延迟解码腾出空间"; the analysis page's
 // row table): NVFP4 row = 256 nibble bytes | 32 E4M3 block scales | 64 E4M3 rope bytes (352 B);
 // FP8 row = 512 E4M3 latent bytes | 64 E4M3 rope bytes (576 B).  Rounding: scale = E4M3 nearest to
 // amax/6, element = e2m1 nearest to |x|/scale, rope and FP8 = E4M3 nearest; ties to the even code,

@@ -91,7 +91,7 @@ def e4m3_value(code) -> float:
 
 
 def e2m1_value(code) -> float:
-    """e2m1 nibble -> value (launch post, NVFP4 KV compression: four bits per value)."""
+    """e2m1 nibble -> value (launch post, making room for low-latency decode: four bits per value)."""
     return _load().mlo_e2m1_value(int(code))
 
 
@@ -122,7 +122,7 @@ def e2m1_encode(bits: np.ndarray, scale: int) -> np.ndarray:
 # --------------------------------------------------------------------------- rows
 
 def quant_row_nvfp4(latent_bits: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
-    """One token -> 352-byte row (launch post, NVFP4 KV compression; analysis, row table)."""
+    """One token -> 352-byte row (launch post, making room for low-latency decode; analysis, row table)."""
     lat = np.ascontiguousarray(latent_bits, dtype=np.uint16).reshape(LATENT)
     rope = np.ascontiguousarray(rope_bits, dtype=np.uint16).reshape(ROPE)
     row = np.zeros(NVFP4_ROW_BYTES, np.uint8)

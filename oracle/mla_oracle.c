@@ -6,10 +6,10 @@
  * under nvfp4_compressed_sparse_amd/, and it includes none of that path's files.
  *
  * What it follows (page titles as in the source pages; no line numbers):
- *  - "Prime Inference" launch post, section "Decode: NVFP4 KV compression" (making room for
- *    low-latency decode): the 512-value MLA latent is stored as NVFP4, four bits per value with one
+ *  - "Prime Inference" launch post (Chinese translation), section "为低延迟解码腾出空间" (making
+ *    room for low-latency decode): the 512-value MLA latent is stored as NVFP4, four bits per value with one
  *    FP8 scale per group of 16 values; the 64-value rope part stays FP8; a row shrinks from 576 to
- *    352 bytes.  Section "Native NVFP4 sparse MLA decode kernel": the decode reads only the rows the
+ *    352 bytes.  Section "原生 NVFP4 稀疏 MLA 解码内核" (native NVFP4 sparse MLA decode kernel): the decode reads only the rows the
  *    sparse indexer selected (at most 2,048 per query token), unpacks them and runs attention with
  *    FP32 accumulation; list entries of -1 are unused slots.
  *  - "Prime Inference: serving GLM-5.3 to agents is a KV-cache problem", section "Four bits per
