@@ -122,7 +122,7 @@ def main():
         ws_bytes = M.mla_sparse_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S)
     else:
         ws_bytes = M.mla_dense_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, int(lay.ctx.max()), S)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # split counters start at zero
     out = torch.empty((cfg.B, cfg.T, cfg.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()

@@ -103,10 +103,13 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
 int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context);
 
-/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): the fp32 partial
- * outputs and log-sum-exps of the splits, merged by a second small launch on the same stream (the
- * pages merge a cluster's partial results without one).  Contents on entry do not matter; two calls
- * that can run concurrently must not share a workspace. */
+/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): per-query-token
+ * split arrival counters, then the fp32 partial outputs and log-sum-exps of the splits.  The last
+ * workgroup of a query token to finish merges its splits in the same launch (the pages merge a
+ * cluster's partial results without a second launch either).
+ * A workspace must be ZERO-FILLED before its first use; every call returns the counters to zero, so
+ * a workspace can then be reused by any later call on the same stream (any shape).  Two calls that can
+ * run concurrently must not share a workspace. */
 size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits);
 
@@ -130,8 +133,8 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *                 into this many parts whose results are merged with their log-sum-exp weights
  *   out           (device) bf16 [B, T, H, 512], 16-byte aligned
  *   lse           (device) fp32 [B, T, H] or NULL
- *   workspace     (device) >= mla_sparse_decode_workspace_bytes(...) bytes, 256-byte aligned; may be
- *                 NULL when that size is 0; contents on entry do not matter
+ *   workspace     (device) >= mla_sparse_decode_workspace_bytes(...) bytes, 256-byte aligned, zero-filled
+ *                 before its first use (see above); may be NULL when that size is 0
  */
 int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,

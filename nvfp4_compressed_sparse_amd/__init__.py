@@ -154,7 +154,7 @@ def _decode_io(q, out, lse, workspace, ws_bytes):
         if tuple(lse.shape) != (B, T, H) or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous [B, T, H] fp32 tensor")
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)  # counters start at zero
     if workspace is not None:
         _dev(workspace, torch.uint8, "workspace")
     return out, lse, workspace

@@ -52,17 +52,20 @@ int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout when S > 1: [partial outputs: B*T*H*S*512 fp32][partial lse: B*T*H*S fp32], each
-// region 256-byte aligned.
+// Workspace layout when S > 1: [split arrival counters: B*T*head groups int32][partial outputs:
+// B*T*H*S*512 fp32][partial lse: B*T*H*S fp32], each region 256-byte aligned.  The counters must be
+// zero before the first call; every call leaves them zero.
 struct WsLayout {
-  size_t o_off, lse_off, total;
+  size_t cnt_off, o_off, lse_off, total;
 };
 
 WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
-  WsLayout l{0, 0, 0};
+  WsLayout l{0, 0, 0, 0};
   if (S <= 1) return l;
   const size_t rows = (size_t)(B * T * H);
-  l.lse_off = round256(rows * (size_t)S * 512 * sizeof(float));
+  const size_t units = (size_t)(B * T * head_groups((int32_t)H));
+  l.o_off = round256(units * sizeof(int32_t));
+  l.lse_off = l.o_off + round256(rows * (size_t)S * 512 * sizeof(float));
   l.total = l.lse_off + round256(rows * (size_t)S * sizeof(float));
   return l;
 }
@@ -149,6 +152,7 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   const WsLayout wl = workspace_layout(B, T, H, S);
   a.part_o = need ? (float*)((char*)workspace + wl.o_off) : nullptr;
   a.part_lse = need ? (float*)((char*)workspace + wl.lse_off) : nullptr;
+  a.counters = need ? (int*)((char*)workspace + wl.cnt_off) : nullptr;
   return mla::launch_decode(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

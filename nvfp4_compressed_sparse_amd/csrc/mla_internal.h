@@ -38,6 +38,7 @@ struct DecodeArgs {
   float* lse;                 // [B,T,H] or nullptr
   float* part_o;              // [B*T*H, S, 512] when S > 1
   float* part_lse;            // [B*T*H, S]
+  int* counters;              // [B*T*head groups] split arrival counters, zero between calls
 };
 
 hipError_t launch_quant(int fmt, const QuantArgs& a, hipStream_t stream);
