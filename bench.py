@@ -57,15 +57,34 @@ def source_hash():
 
 
 def traffic_from_profile(workload: str):
-    """Per-launch HBM bytes measured by rocprofv3 counters, if recorded for the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    """Per-launch HBM bytes (reads + writes) from the rocprofv3 counter summary of this workload's decode
+    kernel, if it was taken on the current kernel source (profiles/decode_<workload>_traffic.md holds
+    lines `source_hash: ...` and `traffic_bytes_per_launch: ...`)."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
     if not os.path.exists(p):
         return None
+    rec = {}
     with open(p) as f:
-        rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip().strip("`")
+    if rec.get("source_hash") != source_hash() or "traffic_bytes_per_launch" not in rec:
         return None
-    return rec.get("bytes_per_launch")
+    return int(float(rec["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size (reads nbytes, writes nbytes), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters of a rocprofv3 --pmc run to bytes."""
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -77,7 +96,12 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in DESIGN.md "
@@ -190,8 +214,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_from_profile(cfg.name)
-    roof["kernel"] = "mla_sparse_decode call (decode_kernel + merge_kernel when split)" if cfg.topk else \
-        "mla_dense_decode_fp8 call (decode_kernel + merge_kernel when split)"
+    roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + \
+        " call: decode_kernel (split merge inside), timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)

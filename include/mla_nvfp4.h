@@ -123,8 +123,9 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *     lse[b][t][h] = ln sum_i e^{z_i}  (natural log);  empty J gives out = 0, lse = -inf.
  *   q             (device) bf16 [B, T, H, 576] contiguous, 16-byte aligned (the absorbed query)
  *   pool          (device) NVFP4 page pool as written by mla_kv_quant_nvfp4; page_stride_bytes as there
- *   block_table   (device) int32, request b's logical page p at block_table[b*bt_stride + p];
- *                 at least ceil(context_lens[b]/64) entries per request are read
+ *   block_table   (device) int32 [B, bt_stride], request b's logical page p at block_table[b*bt_stride + p];
+ *                 all bt_stride entries of each request's row are read (whatever its context length),
+ *                 so the whole B*bt_stride table must be readable
  *   context_lens  (device) int32 [B], tokens in each request's cache (the T query tokens included)
  *   indices       (device) int32 [B, T, topk] logical positions, -1 = unused
  *   B, T          >= 1;  H in {16, 32, 64, 128};  1 <= topk <= 2048
@@ -146,7 +147,8 @@ int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes
  * Dense MLA decode over 576-byte FP8 rows: the same definition with J = {0, ..., limit} (every cached
  * position), the comparison path of the launch post ("FP8 attention").  max_context >= every
  * context_lens[b] (it sizes the grid); other arguments as for mla_sparse_decode, with the pool
- * written by mla_kv_quant_fp8 (page_stride_bytes >= 64*576).
+ * written by mla_kv_quant_fp8 (page_stride_bytes >= 64*576).  Here the entries of block_table that are
+ * read are those of the pages below min(bt_stride, ceil(max_context/64)) in each request's row.
  */
 int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
                          const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens, int32_t B,

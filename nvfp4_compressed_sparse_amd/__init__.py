@@ -168,8 +168,8 @@ def _common(q, pool, block_table, context_lens):
     _dev(context_lens, torch.int32, "context_lens")
     if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, T, H, 576] bf16 tensor")
-    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] != q.shape[0]:
-        raise ValueError("block_table must be [B, pages] with unit inner stride")
+    if block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table must be a contiguous [B, pages] int32 tensor")
     if context_lens.numel() != q.shape[0] or not context_lens.is_contiguous():
         raise ValueError("context_lens must be a contiguous [B] int32 tensor")
 

@@ -52,19 +52,20 @@ constexpr float kLazyRescale = 8.0f;   // log2 headroom of the lazy softmax refe
 constexpr int kPStride = kStepRows * 2 + 16;  // bytes per head of a P tile: 64 FP16 values + padding
 constexpr int kTileStride = kLatent + 4;       // floats per head of a split's result tile in LDS (padded)
 
-// Geometry of the raw-row ring: steps of 64 rows, 8 per wave.  In LDS a row takes one 16-byte chunk
-// more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes of a lane group start
-// on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l of a wave's DMA load u
-// fills LDS chunk 64u+l of the wave's 8 rows; the padding chunks are not loaded.  A step's slot is
-// reused NS steps later; step k is issued during step k-(NS-2).
+// Geometry of the raw-row ring: steps of 64 rows; the four accumulate waves gather 16 rows of each step
+// (the score waves issue no gathers, which evens out the two roles' instruction counts).  In LDS a row
+// takes one 16-byte chunk more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes
+// of a lane group start on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l
+// of a wave's DMA load u fills LDS chunk 64u+l of the wave's 16 rows; the padding chunks are not
+// loaded.  A step's slot is reused NS steps later; step k is issued during step k-(NS-2).
 template <int FMT>
 struct Geo {
   static constexpr int kRowBytes = FMT == 0 ? kNvfp4Row : kFp8Row;
   static constexpr int kChunks = kRowBytes / 16;                 // 22 or 36 per row
   static constexpr int kStride = kRowBytes + 16;                 // LDS bytes per row
-  static constexpr int kWaveRows = kStepRows / kWaves;           // 8
-  static constexpr int kWaveChunks = kWaveRows * (kChunks + 1);  // 184 or 296 LDS chunks per wave per step
-  static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 3 or 5 DMA loads per wave per step
+  static constexpr int kWaveRows = kStepRows / 4;               // 16 rows per gathering wave
+  static constexpr int kWaveChunks = kWaveRows * (kChunks + 1);  // 368 or 592 LDS chunks per wave per step
+  static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 6 or 10 DMA loads per wave per step
   static constexpr int kSlot = kStepRows * kStride;              // bytes of one step
   static constexpr int kSlots = FMT == 0 ? 6 : 3;                // ring depth
   static constexpr int kRing = kSlots * kSlot;
@@ -208,29 +209,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  const int L = a.ctx[b];
-  const int lim = a.causal ? L - a.T + t : L - 1;
-  const int e0 = s * a.chunk;
-  const int e_end = DENSE ? (lim + 1 < a.entries ? lim + 1 : a.entries) : a.entries;
-  const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
-
   // ---- prologue: valid rows of this split -> LDS list of 16-byte row addresses.
-  // The page-table entries this split can touch are staged in LDS with coalesced loads while the
-  // split's list entries load at the same time: one memory round trip instead of two dependent ones.
+  // The page-table entries this split can touch (the request's whole table row for a sparse list, the
+  // pages of the split's position range for a dense one; neither depends on the context length) are
+  // staged in LDS with coalesced loads while the context length and the split's list entries load at
+  // the same time: one memory round trip instead of two or three dependent ones.
+  const int e0 = s * a.chunk;
   const int p0 = DENSE ? (e0 >> 6) : 0;
-  const int p1 = DENSE ? ((e1 - 1) >> 6) : (lim >> 6);
-  const int npg = (e1 > e0 && p1 >= p0) ? p1 - p0 + 1 : 0;
+  int npg = DENSE ? (int)(((int64_t)e0 + a.chunk - 1) / 64 - p0 + 1) : (int)a.bt_stride;
+  if (p0 + npg > a.bt_stride) npg = (int)a.bt_stride - p0;
+  if (npg < 0) npg = 0;
   constexpr int kBtCap = (NS - 2) * G::kSlot / 4;  // below the query staging area
   const bool staged = npg <= kBtCap;
   int* btl = reinterpret_cast<int*>(sh.ring);
   const int* btg = a.block_table + (int64_t)b * a.bt_stride + p0;
-  constexpr int kBtPer = 6;  // entries per thread loaded before any is stored (contexts up to 196,608)
+  constexpr int kBtPer = 6;  // entries per thread loaded before any is stored (tables up to 3,072 pages)
   const bool bt_regs = npg <= kThreads * kBtPer;
   int btv[kBtPer];
   if (bt_regs) {
 #pragma unroll
     for (int k = 0; k < kBtPer; ++k) btv[k] = tid + kThreads * k < npg ? btg[tid + kThreads * k] : 0;
   }
+  const int L = a.ctx[b];
+  const int lim = a.causal ? L - a.T + t : L - 1;
+  const int e_end = DENSE ? (lim + 1 < a.entries ? lim + 1 : a.entries) : a.entries;
+  const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
 
   constexpr int EPT = kEntriesPerThread;
   int pos[EPT];
@@ -267,8 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   uint32_t vmask = 0;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    const bool inr = pos[k] >= 0 && pos[k] <= lim;
-    const int pg = (inr ? pos[k] : 0) >> 6;
+    const int pg = (pos[k] >= 0 ? pos[k] : 0) >> 6;
+    // a position past the limit, or on a page beyond the table width (only with a context longer than
+    // the table allows), selects nothing
+    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg - p0 < npg;
     int page = -1;
     if (inr) page = staged ? btl[pg - p0] : btg[pg - p0];
     const bool ok = inr && page >= 0 && page < a.num_pages;
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   const int nsteps = (n_valid + kStepRows - 1) / kStepRows;
   auto slot_ptr = [&](int st) { return sh.ring + (st % NS) * G::kSlot; };
-  auto issue_step = [&](int st) {
-    const int rb = st * kStepRows + G::kWaveRows * w;
-    const uint8_t* dst = slot_ptr(st) + G::kWaveRows * w * RS;
+  auto issue_step = [&](int st) {  // accumulate waves only
+    const int rb = st * kStepRows + G::kWaveRows * r4;
+    const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int e = 64 * u + lane;  // my LDS chunk of the wave's 8 rows
@@ -346,12 +351,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   };
   // step 0 alone first (its rows arrive sooner when the whole chip is not also fetching the next steps),
   // then the rest of the prefetch window
-  if (nsteps > 0) issue_step(0);
+  if (!scorer && nsteps > 0) issue_step(0);
   wait_vmem();
   lds_barrier();  // step 0 visible; the score waves hold their query fragments (the staging area is reused)
+  if (!scorer) {
 #pragma unroll
-  for (int k = 1; k < NS - 2; ++k)
-    if (k < nsteps) issue_step(k);
+    for (int k = 1; k < NS - 2; ++k)
+      if (k < nsteps) issue_step(k);
+  }
 
   // a split's normalized result tile, [NH][kTileStride] fp32, reuses the ring after the main loop
   float* tile = reinterpret_cast<float*>(sh.ring);
@@ -369,7 +376,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int tt = 0; tt < HT; ++tt) lsum[tt] = 0.0f;
 
     for (int k = 0; k <= nsteps; ++k) {
-      if (k + NS - 2 < nsteps) issue_step(k + NS - 2);  // into the slot of step k-2 (fully consumed)
       float sv[HT][4];
       float psum[HT];  // sum of this lane's speculative P per head tile
       if (k < nsteps) {
@@ -428,8 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             mx = fmaxf(mx, sv[tt][i]);
           }
           raise |= mx > ref[tt] + kLazyRescale;
-          mx = wave_max_xor(mx, 16);
-          mx = wave_max_xor(mx, 32);
+          mx = group4_max(mx);
           if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = mx;
           const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
           float p[4];
@@ -440,8 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         if (__any(raise) && lane == 0) sh.flag[k & 1] = 1;
       }
-      wait_for_step(k + 1);
-      lds_barrier();  // step k's P and flag, step k+1's rows visible
+      lds_barrier();  // step k's P and flag, step k+1's rows (gathered by the accumulate waves) visible
       if (k < nsteps) {
         if (sh.flag[k & 1]) {  // rare: the reference rises; every wave takes this branch
           float alpha[HT];
@@ -466,9 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // softmax sums per head over this wave's rows
 #pragma unroll
     for (int tt = 0; tt < HT; ++tt) {
-      float l = lsum[tt];
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
+      const float l = group4_sum(lsum[tt]);
       if (g == 0) sh.wsum[16 * tt + n][rt] = l;
     }
     wait_vmem();
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const uint32_t vsel = (uint32_t)((n >> 1) & 3) | ((uint32_t)(4 + ((n >> 1) & 3)) << 8);
 
   for (int k = 0; k <= nsteps; ++k) {
-    if (k + NS - 2 < nsteps) issue_step(k + NS - 2);
+    if (k + NS - 2 < nsteps) issue_step(k + NS - 2);  // into the slot of step k-2 (fully consumed)
     if (k >= 1) {
       const uint8_t* slot = slot_ptr(k - 1);
       const uint8_t* pt = sh.ptile[(k - 1) & 1];
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-    wait_for_step(k + 1);
+    wait_for_step(k + 1);  // this wave's rows of step k+1 have landed
     lds_barrier();  // matches the score waves' barrier of step k
     if (k < nsteps && sh.flag[k & 1]) {
       float alpha[HT];
@@ -648,25 +650,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       for (int jj = 0; jj < NP; ++jj) acc[jj] = f32x2{0.0f, 0.0f};
       float Z = 0.0f;
       if (M != -INFINITY) {
-        for (int k = 0; k < S; ++k) {
-          const float lk = k == s ? sh.tile_lse[h] : load_coherent(pl + k);
-          const float wk = __expf(lk - M);
-          Z += wk;
-          if (wk == 0.0f) continue;
-          f32x2 v[NP];
-          if (k == s) {
+        // two splits per round, their loads issued together
+        for (int k0 = 0; k0 < S; k0 += 2) {
+          f32x2 v[2][NP];
+          float wk[2];
 #pragma unroll
-            for (int jj = 0; jj < NP; ++jj) {
-              const int c = cp + 2 * TPH * jj;
-              v[jj] = f32x2{tile[h * kTileStride + c], tile[h * kTileStride + c + 1]};
+          for (int u = 0; u < 2; ++u) {
+            const int k = k0 + u;
+            wk[u] = 0.0f;
+            if (k >= S) continue;
+            wk[u] = __expf((k == s ? sh.tile_lse[h] : load_coherent(pl + k)) - M);
+            if (k == s) {
+#pragma unroll
+              for (int jj = 0; jj < NP; ++jj) {
+                const int c = cp + 2 * TPH * jj;
+                v[u][jj] = f32x2{tile[h * kTileStride + c], tile[h * kTileStride + c + 1]};
+              }
+            } else {
+              const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent);
+#pragma unroll
+              for (int jj = 0; jj < NP; ++jj) v[u][jj] = load_coherent2(src + (cp + 2 * TPH * jj) / 2);
             }
-          } else {
-            const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent);
-#pragma unroll
-            for (int jj = 0; jj < NP; ++jj) v[jj] = load_coherent2(src + (cp + 2 * TPH * jj) / 2);
           }
 #pragma unroll
-          for (int jj = 0; jj < NP; ++jj) acc[jj] += wk * v[jj];
+          for (int u = 0; u < 2; ++u) {
+            Z += wk[u];
+            if (wk[u] == 0.0f) continue;
+#pragma unroll
+            for (int jj = 0; jj < NP; ++jj) acc[jj] += wk[u] * v[u][jj];
+          }
         }
       }
       const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;

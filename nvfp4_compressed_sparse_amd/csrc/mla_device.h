@@ -157,6 +157,21 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups), with the gfx950 lane
+// swaps (VALU, no LDS round trip): swap(x, x) yields the pair {x[l], x[l^32]} (resp. x[l^16]).
+__device__ __forceinline__ float group4_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Workgroup barrier ordering LDS accesses only: this wave's LDS operations complete (lgkmcnt(0)),
 // then s_barrier.  Vector-memory loads still in flight (the next tiles' row gathers into other LDS
 // slots) are not waited for; the "memory" clobber keeps the compiler from moving memory accesses
