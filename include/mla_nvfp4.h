@@ -103,10 +103,10 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
 int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context);
 
-/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): per-query-token
- * split arrival counters, then the fp32 partial outputs and log-sum-exps of the splits.  The last
- * workgroup of a query token to finish merges its splits in the same launch (the pages merge a
- * cluster's partial results without a second launch either).
+/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): one int32
+ * arrival counter per query token and head group, then the FP16 partial outputs and fp32
+ * log-sum-exps of the splits.  The last workgroup of a query token to finish merges its splits in the
+ * same launch (the pages merge a cluster's partial results without a second launch either).
  * A workspace must be ZERO-FILLED before its first use; every call returns the counters to zero, so
  * a workspace can then be reused by any later call on the same stream (any shape).  Two calls that can
  * run concurrently must not share a workspace. */

@@ -65,7 +65,7 @@ WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
   const size_t rows = (size_t)(B * T * H);
   const size_t units = (size_t)(B * T * head_groups((int32_t)H));
   l.o_off = round256(units * sizeof(int32_t));
-  l.lse_off = l.o_off + round256(rows * (size_t)S * 512 * sizeof(float));
+  l.lse_off = l.o_off + round256(rows * (size_t)S * 512 * sizeof(uint16_t));
   l.total = l.lse_off + round256(rows * (size_t)S * sizeof(float));
   return l;
 }
@@ -150,7 +150,7 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   a.out = (uint16_t*)out;
   a.lse = lse;
   const WsLayout wl = workspace_layout(B, T, H, S);
-  a.part_o = need ? (float*)((char*)workspace + wl.o_off) : nullptr;
+  a.part_o = need ? (uint16_t*)((char*)workspace + wl.o_off) : nullptr;
   a.part_lse = need ? (float*)((char*)workspace + wl.lse_off) : nullptr;
   a.counters = need ? (int*)((char*)workspace + wl.cnt_off) : nullptr;
   return mla::launch_decode(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -119,13 +119,15 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t ra, uint32_t rb) {
 }
 
 // Agent-coherent relaxed accesses for the split results exchanged between workgroups.
-__device__ __forceinline__ void store_coherent(uint64_t* p, float lo, float hi) {
-  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Four floats as FP16 (round to nearest even) in one 8-byte agent-coherent store, and back to floats.
+__device__ __forceinline__ void store_coherent_h4(uint64_t* p, f32x4 v) {
+  const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+  const uint64_t x = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ f32x2 load_coherent2(const uint64_t* p) {
-  const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+__device__ __forceinline__ f32x4 h4_to_f32x4(uint64_t x) {
+  const f16x2 lo = __builtin_bit_cast(f16x2, (uint32_t)x), hi = __builtin_bit_cast(f16x2, (uint32_t)(x >> 32));
+  return f32x4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
 }
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -305,26 +307,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   wait_vmem();
   __syncthreads();  // row list and staged queries complete; the page-table staging area is free again
 
-  // query fragments of the score waves (B operand of S^T = K q^T), FP16: lane (g, n) holds head
-  // 16tt+n, latent dims 128g+8ks..+7 (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
-  f16x8 qf[HT][18];
-  if (scorer) {
-#pragma unroll
-    for (int tt = 0; tt < HT; ++tt)
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qstage + 2 * ((16 * tt + n) * kQK + d));
-        f16x2 hv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t dd = raw[k];
-          hv[k] = f16x2{(_Float16)__uint_as_float(dd << 16), (_Float16)__uint_as_float(dd & 0xFFFF0000u)};
-        }
-        qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
-      }
-  }
-
   const int nsteps = (n_valid + kStepRows - 1) / kStepRows;
   auto slot_ptr = [&](int st) { return sh.ring + (st % NS) * G::kSlot; };
   auto issue_step = [&](int st) {  // accumulate waves only
@@ -349,16 +331,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     ahead = ahead < 0 ? 0 : ahead;
     wait_steps<NL>(ahead);
   };
-  // step 0 alone first (its rows arrive sooner when the whole chip is not also fetching the next steps),
-  // then the rest of the prefetch window
-  if (!scorer && nsteps > 0) issue_step(0);
-  wait_vmem();
-  lds_barrier();  // step 0 visible; the score waves hold their query fragments (the staging area is reused)
-  if (!scorer) {
-#pragma unroll
-    for (int k = 1; k < NS - 2; ++k)
-      if (k < nsteps) issue_step(k);
-  }
 
   // a split's normalized result tile, [NH][kTileStride] fp32, reuses the ring after the main loop
   float* tile = reinterpret_cast<float*>(sh.ring);
@@ -370,6 +342,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   if (scorer) {
     // ================= score waves: S^T = K q^T, P = 2^(s - ref) for rows 16rt..16rt+15 of step k
+    // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
+    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
+    f16x8 qf[HT][18];
+#pragma unroll
+    for (int tt = 0; tt < HT; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qstage + 2 * ((16 * tt + n) * kQK + d));
+        f16x2 hv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t dd = raw[k];
+          hv[k] = f16x2{(_Float16)__uint_as_float(dd << 16), (_Float16)__uint_as_float(dd & 0xFFFF0000u)};
+        }
+        qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
+      }
+    lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
     const int rt = r4;
     float lsum[HT];
 #pragma unroll
@@ -477,6 +467,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
+  // The prefetch window below the query staging slots is issued at once, so the first memory round
+  // trip of the gathers brings NS-2 steps rather than one; only step 0 is awaited before the barrier.
+  {
+#pragma unroll
+    for (int k = 0; k < NS - 2; ++k)
+      if (k < nsteps) issue_step(k);
+    const int inflight = (nsteps < NS - 2 ? nsteps : NS - 2) - 1;
+    wait_steps<NL>(inflight > 0 ? inflight : 0);
+  }
+  lds_barrier();  // step 0 visible; the score waves hold their query fragments
   const int cq = r4;
   f32x4 o[HT][8];  // O^T tile c: O[head 16t+n][column 128cq+32g+8i+c] = o[t][c][i]
 #pragma unroll
@@ -613,26 +613,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // the same launch; here the last workgroup of a query token to finish merges them): lse = M + ln
   // sum_s e^{lse_s - M}, out = sum_s e^{lse_s - lse} out_s; a split with no rows has lse_s = -inf and no
   // weight; all splits empty -> out = 0, lse = -inf.  The arrival counter returns to zero.
-  // Split results travel through agent-coherent (L2-bypassing) relaxed accesses, so no device-scope
-  // fence (which writes back and invalidates the whole L2) is needed: the stores are complete (vmcnt 0)
-  // before the arrival counter moves, and the merging workgroup reads only after it saw the last
-  // arrival.  Thread tid owns head h = tid / TPH and the column pairs 2*(tid % TPH) + 2*TPH*j, so each
-  // load or store instruction covers whole cache lines.
+  // Each workgroup stores its normalized result (FP16, far below the bf16 output's rounding) and lse
+  // with agent-coherent (L2-bypassing) relaxed stores, waits until they are complete (vmcnt 0) and only
+  // then moves the arrival counter; the workgroup that moves it to S merges, reading with coherent
+  // loads.  No device-scope fence (which writes back and invalidates the whole L2) is needed.  Thread
+  // tid owns head h = tid / TPH and the column quads 4*(tid % TPH) + 4*TPH*j, so each load or store
+  // instruction covers whole cache lines.
   if (S > 1) {
     constexpr int TPH = kThreads / NH;        // threads per head: 16 or 32
-    constexpr int NP = kLatent / (2 * TPH);   // column pairs per thread: 16 or 8
+    constexpr int NQ = kLatent / (4 * TPH);   // column quads per thread: 8 or 4
     const int h = tid / TPH;
-    const int cp = 2 * (tid % TPH);
+    const int c4 = 4 * (tid % TPH);
     const int64_t hrow = (int64_t)qtok * a.H + h0 + h;
+    const float* own = tile + h * kTileStride + c4;
     __syncthreads();  // the result tile and its lse are complete
     {
-      uint64_t* dst = reinterpret_cast<uint64_t*>(a.part_o + (hrow * S + s) * kLatent);
-      const float* src = tile + h * kTileStride;
+      uint64_t* dst = reinterpret_cast<uint64_t*>(a.part_o + (hrow * S + s) * kLatent + c4);
 #pragma unroll
-      for (int jj = 0; jj < NP; ++jj) {
-        const int c = cp + 2 * TPH * jj;
-        store_coherent(dst + c / 2, src[c], src[c + 1]);
-      }
+      for (int jj = 0; jj < NQ; ++jj)
+        store_coherent_h4(dst + TPH * jj, *reinterpret_cast<const f32x4*>(own + 4 * TPH * jj));
       if (tid % TPH == 0) __hip_atomic_store(a.part_lse + hrow * S + s, sh.tile_lse[h], __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -642,50 +641,54 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     if (tid == 0) sh.last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
     if (sh.last) {
+      // running merge: the own split from LDS, then the others four per round with every load of a
+      // round (results and lse) issued together
+      float M = sh.tile_lse[h];
+      float Z = M == -INFINITY ? 0.0f : 1.0f;
+      f32x4 acc[NQ];
+#pragma unroll
+      for (int jj = 0; jj < NQ; ++jj)
+        acc[jj] = M == -INFINITY ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const f32x4*>(own + 4 * TPH * jj);
       const float* pl = a.part_lse + hrow * S;
-      float M = -INFINITY;
-      for (int k = 0; k < S; ++k) M = fmaxf(M, k == s ? sh.tile_lse[h] : load_coherent(pl + k));
-      f32x2 acc[NP];
+      for (int k0 = 0; k0 < S; k0 += 4) {
+        float lk[4];
+        uint64_t raw[4][NQ];
 #pragma unroll
-      for (int jj = 0; jj < NP; ++jj) acc[jj] = f32x2{0.0f, 0.0f};
-      float Z = 0.0f;
-      if (M != -INFINITY) {
-        // two splits per round, their loads issued together
-        for (int k0 = 0; k0 < S; k0 += 2) {
-          f32x2 v[2][NP];
-          float wk[2];
+        for (int u = 0; u < 4; ++u) {
+          const int k = k0 + u;
+          lk[u] = -INFINITY;
+          if (k >= S || k == s) continue;
+          lk[u] = load_coherent(pl + k);
+          const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent + c4);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int k = k0 + u;
-            wk[u] = 0.0f;
-            if (k >= S) continue;
-            wk[u] = __expf((k == s ? sh.tile_lse[h] : load_coherent(pl + k)) - M);
-            if (k == s) {
-#pragma unroll
-              for (int jj = 0; jj < NP; ++jj) {
-                const int c = cp + 2 * TPH * jj;
-                v[u][jj] = f32x2{tile[h * kTileStride + c], tile[h * kTileStride + c + 1]};
-              }
-            } else {
-              const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent);
-#pragma unroll
-              for (int jj = 0; jj < NP; ++jj) v[u][jj] = load_coherent2(src + (cp + 2 * TPH * jj) / 2);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            Z += wk[u];
-            if (wk[u] == 0.0f) continue;
-#pragma unroll
-            for (int jj = 0; jj < NP; ++jj) acc[jj] += wk[u] * v[u][jj];
-          }
+          for (int jj = 0; jj < NQ; ++jj)
+            raw[u][jj] = __hip_atomic_load(const_cast<uint64_t*>(src + TPH * jj), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
         }
+        const float mnew = fmaxf(fmaxf(M, fmaxf(lk[0], lk[1])), fmaxf(lk[2], lk[3]));
+        if (mnew == -INFINITY) continue;
+        const float r = __expf(M - mnew);  // 0 while M = -inf
+        Z *= r;
+#pragma unroll
+        for (int jj = 0; jj < NQ; ++jj) acc[jj] *= r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (lk[u] == -INFINITY) continue;
+          const float wk = __expf(lk[u] - mnew);
+          Z += wk;
+#pragma unroll
+          for (int jj = 0; jj < NQ; ++jj) acc[jj] += wk * h4_to_f32x4(raw[u][jj]);
+        }
+        M = mnew;
       }
       const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + hrow * kLatent);
+      u32x2* dst = reinterpret_cast<u32x2*>(a.out + hrow * kLatent + c4);
 #pragma unroll
-      for (int jj = 0; jj < NP; ++jj) dst[(cp + 2 * TPH * jj) / 2] = pack_bf16_rne(acc[jj][0] * inv, acc[jj][1] * inv);
-      if (tid % TPH == 0 && a.lse) a.lse[hrow] = M == -INFINITY ? -INFINITY : M + __logf(Z);
+      for (int jj = 0; jj < NQ; ++jj) {
+        const f32x4 v = acc[jj] * inv;
+        dst[TPH * jj] = u32x2{pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3])};
+      }
+      if (tid % TPH == 0 && a.lse) a.lse[hrow] = Z > 0.0f ? M + __logf(Z) : -INFINITY;
       if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

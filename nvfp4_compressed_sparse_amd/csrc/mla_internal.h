@@ -36,7 +36,7 @@ struct DecodeArgs {
   float scale_log2;           // sm_scale * log2(e)
   uint16_t* out;              // bf16 [B,T,H,512]
   float* lse;                 // [B,T,H] or nullptr
-  float* part_o;              // [B*T*H, S, 512] when S > 1
+  uint16_t* part_o;           // FP16 [B*T*H, S, 512] when S > 1
   float* part_lse;            // [B*T*H, S]
   int* counters;              // [B*T*head groups] split arrival counters, zero between calls
 };

@@ -127,10 +127,11 @@ def test_split_choice_and_workspace_sizes():
     assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 1) == 0
     rows = 64 * 32
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # split arrival counters (one per query token and 32-head group) + fp32 partial outputs + partial lse
-    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 4) == (r256(64 * 4) + r256(rows * 4 * 512 * 4) +
+    # a split counter per query token and 32-head group + FP16 partial outputs + fp32 partial lse
+    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 4) == (r256(64 * 4) + r256(rows * 4 * 512 * 2) +
                                                                        r256(rows * 4 * 4))
-    assert L.mla_sparse_decode_workspace_bytes(8, 1, 128, 2048, 2) == (r256(8 * 4 * 4) + r256(8 * 128 * 2 * 512 * 4) +
+    assert L.mla_sparse_decode_workspace_bytes(8, 1, 128, 2048, 2) == (r256(8 * 4 * 4) +
+                                                                       r256(8 * 128 * 2 * 512 * 2) +
                                                                        r256(8 * 128 * 2 * 4))
 
 
