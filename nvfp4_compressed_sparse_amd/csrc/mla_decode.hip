@@ -66,6 +66,7 @@ struct Geo {
   static constexpr int kWaveRows = kStepRows / 4;               // 16 rows per gathering wave
   static constexpr int kWaveChunks = kWaveRows * (kChunks + 1);  // 368 or 592 LDS chunks per wave per step
   static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 6 or 10 DMA loads per wave per step
+  static_assert((kLoads - 1) * 64 < kWaveChunks, "only a wave's last gather load is partial");
   static constexpr int kSlot = kStepRows * kStride;              // bytes of one step
   static constexpr int kSlots = FMT == 0 ? 6 : 3;                // ring depth
   static constexpr int kRing = kSlots * kSlot;
@@ -312,16 +313,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   auto issue_step = [&](int st) {  // accumulate waves only
     const int rb = st * kStepRows + G::kWaveRows * r4;
     const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
+    // lane l of load u fills LDS chunk e = 64u + l of the wave's rows: chunk c of row e / (kChunks + 1).
+    // Every row address is read first (one LDS round trip), then the loads go out.  The chunk after a
+    // row's last one is the row's padding: it receives the row's first chunk again, so that only the
+    // lanes past the wave's last row (in its last load) are masked.
+    uint32_t a16[NL];
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int e = 64 * u + lane;  // my LDS chunk of the wave's 8 rows
-      const int row = e / (G::kChunks + 1);
-      const int c = e - row * (G::kChunks + 1);
-      if (e < G::kWaveChunks && c < G::kChunks) {
-        const int r = rb + row;
-        const uint32_t a16 = sh.rowlist[r < n_valid ? r : 0];
-        dma16(a.pool + (uint64_t)a16 * 16u + 16 * c, dst + 1024 * u);
-      }
+      const int r = rb + (64 * u + lane) / (G::kChunks + 1);
+      a16[u] = sh.rowlist[r < n_valid ? r : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int e = 64 * u + lane;
+      const int c = e % (G::kChunks + 1);
+      const uint8_t* src = a.pool + (uint64_t)a16[u] * 16u + (c < G::kChunks ? 16 * c : 0);
+      if (u < NL - 1 || e < G::kWaveChunks) dma16(src, dst + 1024 * u);
     }
   };
   // wait until this wave's rows of step k are in LDS (steps after k may still be in flight)
@@ -493,26 +500,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     if (k >= 1) {
       const uint8_t* slot = slot_ptr(k - 1);
       const uint8_t* pt = sh.ptile[(k - 1) & 1];
+      // every LDS read of the step first (P of both contraction halves, V words of the 16 rows this
+      // lane feeds), then the conversions and products
+      f16x8 pb[2][HT];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        f16x8 pb[HT];
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt)
-          pb[tt] = *reinterpret_cast<const f16x8*>(pt + (16 * tt + n) * kPStride + 2 * (32 * kk + 8 * g));
-        // rows pv_row(kk, g, 2p) and the next one feed contraction elements 8g + 2p, 8g + 2p + 1
-        if constexpr (FMT == 0) {
+          pb[kk][tt] = *reinterpret_cast<const f16x8*>(pt + (16 * tt + n) * kPStride + 2 * (32 * kk + 8 * g));
+      // rows pv_row(kk, g, 2p) and the next one feed contraction elements 8g + 2p, 8g + 2p + 1
+      if constexpr (FMT == 0) {
+        uint32_t da[2][4], db[2][4], sa[2][4], sb[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint8_t* ra = slot + pv_row(kk, g, 2 * p) * RS;
+            da[kk][p] = *reinterpret_cast<const uint32_t*>(ra + vcol);
+            sa[kk][p] = *reinterpret_cast<const uint32_t*>(ra + vsc);
+            db[kk][p] = *reinterpret_cast<const uint32_t*>(ra + RS + vcol);
+            sb[kk][p] = *reinterpret_cast<const uint32_t*>(ra + RS + vsc);
+          }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
           uint32_t ev[4][2];
           f16x2 sp[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const uint8_t* ra = slot + pv_row(kk, g, 2 * p) * RS;
-            const uint32_t da = *reinterpret_cast<const uint32_t*>(ra + vcol);
-            const uint32_t db = *reinterpret_cast<const uint32_t*>(ra + RS + vcol);
-            const uint32_t sa = *reinterpret_cast<const uint32_t*>(ra + vsc);
-            const uint32_t sb = *reinterpret_cast<const uint32_t*>(ra + RS + vsc);
-            sp[p] = e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sb, sa, vsel));
-            ev[p][0] = nib_pair<0>(da, db);
-            ev[p][1] = nib_pair<1>(da, db);
+            sp[p] = e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sb[kk][p], sa[kk][p], vsel));
+            ev[p][0] = nib_pair<0>(da[kk][p], db[kk][p]);
+            ev[p][1] = nib_pair<1>(da[kk][p], db[kk][p]);
           }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
@@ -531,20 +548,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             }
             const f16x8 A = as_f16x8(v[0], v[1], v[2], v[3]);
 #pragma unroll
-            for (int tt = 0; tt < HT; ++tt) o[tt][c] = mfma16x16x32(A, pb[tt], o[tt][c]);
+            for (int tt = 0; tt < HT; ++tt) o[tt][c] = mfma16x16x32(A, pb[kk][tt], o[tt][c]);
           }
-        } else {
-          // FP8: byte interleave (row a, row b) per column with v_perm, then exact FP8 -> FP16 pairs
-          uint32_t x[4][4];  // x[p][q]: columns 2q, 2q+1 of rows (a, b) as bytes a, b, a', b'
+        }
+      } else {
+        // FP8: byte interleave (row a, row b) per column with v_perm, then exact FP8 -> FP16 pairs
+        u32x2 da[2][4], db[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const uint8_t* ra = slot + pv_row(kk, g, 2 * p) * RS;
-            const u32x2 da = *reinterpret_cast<const u32x2*>(ra + vcol);
-            const u32x2 db = *reinterpret_cast<const u32x2*>(ra + RS + vcol);
-            x[p][0] = __builtin_amdgcn_perm(db[0], da[0], 0x05010400u);
-            x[p][1] = __builtin_amdgcn_perm(db[0], da[0], 0x07030602u);
-            x[p][2] = __builtin_amdgcn_perm(db[1], da[1], 0x05010400u);
-            x[p][3] = __builtin_amdgcn_perm(db[1], da[1], 0x07030602u);
+            da[kk][p] = *reinterpret_cast<const u32x2*>(ra + vcol);
+            db[kk][p] = *reinterpret_cast<const u32x2*>(ra + RS + vcol);
+          }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          uint32_t x[4][4];  // x[p][q]: columns 2q, 2q+1 of rows (a, b) as bytes a, b, a', b'
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            x[p][0] = __builtin_amdgcn_perm(db[kk][p][0], da[kk][p][0], 0x05010400u);
+            x[p][1] = __builtin_amdgcn_perm(db[kk][p][0], da[kk][p][0], 0x07030602u);
+            x[p][2] = __builtin_amdgcn_perm(db[kk][p][1], da[kk][p][1], 0x05010400u);
+            x[p][3] = __builtin_amdgcn_perm(db[kk][p][1], da[kk][p][1], 0x07030602u);
           }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
               v[p] = (c & 1) ? e4m3x2_to_f16<true>(x[p][c >> 1]) : e4m3x2_to_f16<false>(x[p][c >> 1]);
             const f16x8 A = as_f16x8(v[0], v[1], v[2], v[3]);
 #pragma unroll
-            for (int tt = 0; tt < HT; ++tt) o[tt][c] = mfma16x16x32(A, pb[tt], o[tt][c]);
+            for (int tt = 0; tt < HT; ++tt) o[tt][c] = mfma16x16x32(A, pb[kk][tt], o[tt][c]);
           }
         }
       }
