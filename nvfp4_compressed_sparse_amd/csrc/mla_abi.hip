@@ -50,10 +50,25 @@ int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
   return (int)s;
 }
 
+// The wide-head kernel (64 or 128 heads) runs one workgroup per (query token, split) for every head,
+// so one split result is H x 512 values and the merging workgroup reads S-1 of them: its split count
+// stays small (at most 8, and at least 256 list entries per split).
+constexpr int kWideMaxSplits = 8;
+constexpr int kWideMinEntries = 256;
+
+int auto_splits_wide(int64_t units, int64_t entries) {
+  int64_t s = ceil_div(kTargetWorkgroups, units);
+  int64_t cap = ceil_div(entries, kWideMinEntries);
+  if (cap > kWideMaxSplits) cap = kWideMaxSplits;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout when S > 1: [split arrival counters: B*T*head groups int32][partial outputs:
-// B*T*H*S*512 fp32][partial lse: B*T*H*S fp32], each region 256-byte aligned.  The counters must be
+// B*T*H*S*512 fp16][partial lse: B*T*H*S fp32], each region 256-byte aligned.  The counters must be
 // zero before the first call; every call leaves them zero.
 struct WsLayout {
   size_t cnt_off, o_off, lse_off, total;
@@ -191,6 +206,7 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
 
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk) {
   if (B < 1 || T < 1 || !valid_heads(H) || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  if (mla::uses_wide_kernel(0, H)) return auto_splits_wide((int64_t)B * T, topk);
   return auto_splits((int64_t)B * T * head_groups(H), topk, 1);
 }
 

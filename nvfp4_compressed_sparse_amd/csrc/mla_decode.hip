@@ -77,63 +77,6 @@ struct Geo {
 // dwords mod 64), and (j, j+1) = (2p, 2p+1) are neighbouring rows.  P is stored in the same order.
 __device__ __forceinline__ int pv_row(int kk, int g, int j) { return 16 * (j >> 1) + 4 * g + 2 * kk + (j & 1); }
 
-// LDS-DMA of 16 bytes per lane: lane l's global bytes land at lds + 16*l (lds must be wave-uniform).
-// Issued through asm so that the compiler's waitcnt tracking does not drain the gathers still in
-// flight; completion is awaited explicitly with vmcnt.  M0 is saved and restored around the load.
-__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(m)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((uint16_t)((N & 15) | ((N >> 4) << 14) | 0x0F70));
-}
-
-// Wait until at most k steps of this wave's gathers (NL loads each) are still in flight, 0 <= k <= 4.
-template <int NL>
-__device__ __forceinline__ void wait_steps(int k) {
-  switch (k) {
-    case 0: wait_vmem_le<0>(); break;
-    case 1: wait_vmem_le<NL>(); break;
-    case 2: wait_vmem_le<2 * NL>(); break;
-    case 3: wait_vmem_le<3 * NL>(); break;
-    default: wait_vmem_le<4 * NL>(); break;
-  }
-}
-
-// Byte interleave of two rows' nibble dwords: byte k of the result holds (lo nibble, hi nibble) =
-// (row a, row b) of column 2k (ODD = 0) or 2k+1 (ODD = 1).
-template <int ODD>
-__device__ __forceinline__ uint32_t nib_pair(uint32_t ra, uint32_t rb) {
-  constexpr uint32_t M = 0x0F0F0F0Fu;
-  return ODD ? (((ra >> 4) & M) | (rb & ~M)) : ((ra & M) | ((rb << 4) & ~M));
-}
-
-// Agent-coherent relaxed accesses for the split results exchanged between workgroups.
-// Four floats as FP16 (round to nearest even) in one 8-byte agent-coherent store, and back to floats.
-__device__ __forceinline__ void store_coherent_h4(uint64_t* p, f32x4 v) {
-  const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
-  const uint64_t x = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x4 h4_to_f32x4(uint64_t x) {
-  const f16x2 lo = __builtin_bit_cast(f16x2, (uint32_t)x), hi = __builtin_bit_cast(f16x2, (uint32_t)(x >> 32));
-  return f32x4{(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // P (FP16) of rows 16rt+4g+i (i < 4) of one head into its P-tile row, in the contraction order of
 // pv_row: row 16a+4g+2kk+e sits at position 32kk+8g+2a+e.
 __device__ __forceinline__ void write_p(uint8_t* prow, int rt, int g, const float (&p)[4]) {
@@ -729,6 +672,7 @@ static void launch_one(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream) {
   const bool dense = a.indices == nullptr;
+  if (uses_wide_kernel(fmt, a.H)) return launch_decode_wide(fmt, a, stream);
   if (fmt == 0) {
     if (a.H == 16) launch_one<1, 0, false>(a, stream);
     else launch_one<2, 0, false>(a, stream);

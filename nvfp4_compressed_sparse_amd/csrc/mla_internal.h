@@ -41,7 +41,13 @@ struct DecodeArgs {
   int* counters;              // [B*T*head groups] split arrival counters, zero between calls
 };
 
+// Which decode kernel serves a shape: the wide-head kernel for NVFP4 rows with 64 or 128 heads (every
+// row dequantized once for all heads), the 16/32-head-group kernel otherwise.
+inline bool uses_wide_kernel(int fmt, int H) { return fmt == 0 && (H == 64 || H == 128); }
+
 hipError_t launch_quant(int fmt, const QuantArgs& a, hipStream_t stream);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream);
+// 64 or 128 heads: one workgroup per (query token, split) covers every head (mla_decode_wide.hip).
+hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -154,15 +154,52 @@ def test_sparse_decode_tiny_config():
     say(compare_outputs(out, ro, lse, rl, "tiny"))
 
 
+@pytest.mark.parametrize("H", [32, 128])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 64])
-def test_sparse_decode_split_counts(S):
-    case = Case(small(H=32, topk=300, L=5000, seed=13))  # 300 = 4 full tiles + a ragged 44
-    say(f"split count {S}")
+def test_sparse_decode_split_counts(S, H):
+    # 300 entries: 4 full 64-row steps + a ragged 44 (16/32 heads), 9 full 32-row steps + 12 (64/128)
+    case = Case(small(H=H, topk=300, L=5000, seed=13))
+    say(f"split count {S} H={H}")
     d = case.to_device()
     gpu_pool(case, d)
     out, lse = gpu_decode(case, d, num_splits=S)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, f"S={S}"))
+    say(compare_outputs(out, ro, lse, rl, f"S={S} H={H}"))
+
+
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("H", [32, 128])
+@pytest.mark.parametrize("pattern", ["rising", "steep", "late_jump", "huge_jump"])
+@pytest.mark.parametrize("S", [1, 2])
+def test_softmax_reference_rises(H, pattern, S):
+    """Scores that grow along the index list make the running softmax reference rise step after step
+    ('rising': about 10 in log2 units per 32 rows; 'steep': about 33) or once at the very end
+    ('late_jump': by about 66, 'huge_jump': by about 266), so the accumulated output is rescaled
+    inside the kernel (the 16/32-head kernel rises past 8 log2 units, the 64/128-head kernel past 100).
+    The query's latent part is zero and its rope part one, so a row's score is sm_scale times the sum
+    of its rope values, which the test sets."""
+    cfg = small(B=2, H=H, topk=256, L=3000, seed=41)
+    case = Case(cfg)
+    off = np.concatenate([[0], np.cumsum(case.lay.ctx)[:-1]])
+    for b in range(cfg.B):
+        pos = case.idx[b, 0]
+        if pattern in ("rising", "steep"):
+            r = np.arange(pos.size) * ((1.5 if pattern == "rising" else 5.0) / 32)
+        else:
+            r = np.zeros(pos.size)
+            r[-5:] = 10.0 if pattern == "late_jump" else 40.0
+        case.rope[off[b] + pos] = _bf16_bits(r)[:, None]
+    case.q[..., :512] = 0
+    case.q[..., 512:] = _bf16_bits(1.0)
+    say(f"reference rises: {pattern} H={H} S={S}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d, num_splits=S)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"{pattern} H={H} S={S}"))
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
