@@ -47,31 +47,38 @@ def algorithmic_work(cfg, valid_rows: int):
     return rows_bytes + qo_bytes + list_bytes, flops
 
 
-def source_hash():
+def uses_wide_kernel(cfg) -> bool:
+    """The library serves NVFP4 rows with 64 or 128 heads with its wide-head decode kernel."""
+    return cfg.fmt == "nvfp4" and cfg.H in (64, 128)
+
+
+def source_hash(cfg):
+    """Hash of the sources of the decode kernel this workload runs (shared headers and the ABI included)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_compressed_sparse_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    kernel = "mla_decode_wide.hip" if uses_wide_kernel(cfg) else "mla_decode.hip"
+    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", kernel):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """Per-launch HBM bytes (reads + writes) from the rocprofv3 counter summary of this workload's decode
-    kernel, if it was taken on the current kernel source (profiles/decode_<workload>_traffic.md holds
-    lines `source_hash: ...` and `traffic_bytes_per_launch: ...`)."""
-    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+def profile_record(cfg, kind: str, key: str):
+    """A figure from a rocprofv3 counter summary of this workload's decode kernel, if it was taken on the
+    current kernel source: profiles/decode_<workload>_<kind>.md holds lines `source_hash: ...` and
+    `<key>: ...`."""
+    p = os.path.join(ROOT, "profiles", f"decode_{cfg.name}_{kind}.md")
     if not os.path.exists(p):
         return None
     rec = {}
     with open(p) as f:
         for line in f:
-            if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", "traffic_bytes_per_launch"):
+            if ":" in line and line.split(":", 1)[0].strip() in ("source_hash", key):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip().strip("`")
-    if rec.get("source_hash") != source_hash() or "traffic_bytes_per_launch" not in rec:
+    if rec.get("source_hash") != source_hash(cfg) or key not in rec:
         return None
-    return int(float(rec["traffic_bytes_per_launch"]))
+    return float(rec[key])
 
 
 def copy_calibration(nbytes: int, reps: int):
@@ -213,9 +220,13 @@ def main():
         ach = flops_per / (dec_avg_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = traffic_from_profile(cfg.name)
-    roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + \
-        " call: decode_kernel (split merge inside), timed with HIP events on its stream"
+    t = profile_record(cfg, "traffic", "traffic_bytes_per_launch")
+    roof["traffic"] = None if t is None else int(t)
+    if cfg.H > 32:
+        roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent")
+    roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + " call: " + \
+        ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
+        " (split merge inside), timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)
