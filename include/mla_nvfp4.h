@@ -129,6 +129,7 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *   context_lens  (device) int32 [B], tokens in each request's cache (the T query tokens included)
  *   indices       (device) int32 [B, T, topk] logical positions, -1 = unused
  *   B, T          >= 1;  H in {16, 32, 64, 128};  1 <= topk <= 2048
+ *   sm_scale      > 0 and finite (the softmax scale, 1/sqrt(192) for the pages' model)
  *   causal        0 or 1 (the T query tokens are the last T positions of the request)
  *   num_splits    0 = the library's choice, else 1..64: the selected rows of each query token are split
  *                 into this many parts whose results are merged with their log-sum-exp weights

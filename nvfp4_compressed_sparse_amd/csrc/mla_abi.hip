@@ -119,7 +119,7 @@ int check_decode_common(const void* q, const void* pool, int64_t page_stride, in
   if (!q || !pool || !block_table || !ctx || !out) return MLA_ERR_NULL;
   if (B < 1 || T < 1 || !valid_heads(H) || num_pages < 1 || bt_stride < 1) return MLA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
-  if (!(sm_scale == sm_scale)) return MLA_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return MLA_ERR_SHAPE;  // a softmax scale: positive, finite
   if ((int64_t)B * T * H * 576 > ((int64_t)1 << 40)) return MLA_ERR_SHAPE;
   if (page_stride < 64LL * row_bytes || page_stride % 16) return MLA_ERR_STRIDE_ALIGN;
   // row addresses travel as 32-bit multiples of 16 bytes

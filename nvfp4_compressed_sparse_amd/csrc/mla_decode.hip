@@ -16,8 +16,8 @@
 //     are validated (index < 0, past the causal limit, or on a page-table entry outside the pool ->
 //     dropped, which also skips their loads) and compacted into an LDS list of row addresses (order
 //     kept, so results are deterministic).
-//   * rows are consumed in steps of 64; every wave gathers 8 rows of each step by LDS-DMA (16 bytes per
-//     lane, no registers) into a ring of raw row slots, several steps ahead.
+//   * rows are consumed in steps of 64; the score waves gather them by LDS-DMA (16 bytes per lane, no
+//     registers) into a ring of raw row slots, several steps ahead.
 //   * the waves specialise, as the pages' warp groups do: waves 0-3 score, waves 4-7 accumulate, one of
 //     each per SIMD, so each SIMD interleaves a scoring and an accumulating wave.  The two roles work one
 //     step apart and meet at one workgroup barrier per step.
@@ -28,9 +28,9 @@
 //     and writes it to LDS as FP16.
 //   * lazy, speculative softmax reference: ref (per head) is shared by all waves and changes only when
 //     a score exceeds it by more than 2^8 (so P stays below 256).  A score wave that sees such a score
-//     raises a flag; after the barrier every wave reads the flag and, in that rare case, all of them
-//     derive the new reference from the per-wave maxima, the accumulators are rescaled and the score
-//     waves rewrite P before one extra barrier.
+//     raises a flag and publishes its per-head maxima; after the barrier every wave reads the flag and,
+//     in that rare case, all of them derive the new reference from the published maxima, the
+//     accumulators are rescaled and the score waves rewrite P before one extra barrier.
 //   * accumulate wave cq computes O^T += V^T P^T for step k-1 over output columns 128cq..128cq+127 and
 //     all heads.  Lane (g, m) reads, for 8 rows, the nibble dword holding columns 128cq+8m..+7 and feeds
 //     column 128cq+8m+c to MFMA tile c (c < 8); the nibbles of two rows are interleaved with bit
@@ -51,9 +51,11 @@ constexpr int kEntriesPerThread = kMaxChunk / kThreads;
 constexpr float kLazyRescale = 8.0f;   // log2 headroom of the lazy softmax reference
 constexpr int kPStride = kStepRows * 2 + 16;  // bytes per head of a P tile: 64 FP16 values + padding
 constexpr int kTileStride = kLatent + 4;       // floats per head of a split's result tile in LDS (padded)
+constexpr int kPrologueSteps = 3;              // steps gathered before step 0 is awaited
 
-// Geometry of the raw-row ring: steps of 64 rows; the four accumulate waves gather 16 rows of each step
-// (the score waves issue no gathers, which evens out the two roles' instruction counts).  In LDS a row
+// Geometry of the raw-row ring: steps of 64 rows; each of the four score waves gathers 16 rows of each
+// step (the accumulate waves have the longer instruction stream per step, so the score waves, which
+// would otherwise wait at the step barrier, take the gathers).  In LDS a row
 // takes one 16-byte chunk more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes
 // of a lane group start on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l
 // of a wave's DMA load u fills LDS chunk 64u+l of the wave's 16 rows; the padding chunks are not
@@ -210,6 +212,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int i = tid; i < npg; i += kThreads) btl[i] = btg[i];
   }
   if (tid < 2) sh.flag[tid] = 0;
+  // published maxima start at -inf: a raise takes the largest published value, and only waves that
+  // raise publish (every score a wave saw before stays within 2^8 of the reference it left behind)
+  if (tid < 2 * NH * 4) (&sh.smax[0][0][0])[tid] = -INFINITY;
   __syncthreads();  // staged page-table entries visible
 
   uint32_t addr[EPT];
@@ -247,39 +252,56 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < EPT; ++k)
     if (vmask & (1u << k)) sh.rowlist[off++] = addr[k];
+  // the list is padded to whole steps with the pool's first row, so that gathers need no bounds
+  // checks (the scores of the padding rows are masked)
+  if (tid < ((n_valid + kStepRows - 1) & -kStepRows) - n_valid) sh.rowlist[n_valid + tid] = 0u;
   // every load issued so far (indices, page table, the query DMA) has landed before the gathers start
   wait_vmem();
   __syncthreads();  // row list and staged queries complete; the page-table staging area is free again
 
   const int nsteps = (n_valid + kStepRows - 1) / kStepRows;
   auto slot_ptr = [&](int st) { return sh.ring + (st % NS) * G::kSlot; };
-  auto issue_step = [&](int st) {  // accumulate waves only
-    const int rb = st * kStepRows + G::kWaveRows * r4;
+  // lane l of gather load u fills LDS chunk e = 64u + l of the wave's rows: chunk c of row e / (kChunks
+  // + 1).  The chunk after a row's last one is the row's padding: it receives the row's first chunk
+  // again, so that only the lanes past the wave's last row (in its last load) are masked.  Per lane and
+  // load: the row within the wave's rows and the byte offset of the chunk.
+  int g_row[NL];
+  uint32_t g_off[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int e = (64 * u + lane) < G::kWaveChunks ? 64 * u + lane : G::kWaveChunks - 1;
+    const int c = e % (G::kChunks + 1);
+    g_row[u] = e / (G::kChunks + 1);
+    g_off[u] = c < G::kChunks ? 16u * c : 0u;
+  }
+  auto issue_step = [&](int st) {  // score waves only
+    const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
     const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
-    // lane l of load u fills LDS chunk e = 64u + l of the wave's rows: chunk c of row e / (kChunks + 1).
-    // Every row address is read first (one LDS round trip), then the loads go out.  The chunk after a
-    // row's last one is the row's padding: it receives the row's first chunk again, so that only the
-    // lanes past the wave's last row (in its last load) are masked.
+    // every row address is read first (one LDS round trip), then the loads go out
     uint32_t a16[NL];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int r = rb + (64 * u + lane) / (G::kChunks + 1);
-      a16[u] = sh.rowlist[r < n_valid ? r : 0];
-    }
+    for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int e = 64 * u + lane;
-      const int c = e % (G::kChunks + 1);
-      const uint8_t* src = a.pool + (uint64_t)a16[u] * 16u + (c < G::kChunks ? 16 * c : 0);
-      if (u < NL - 1 || e < G::kWaveChunks) dma16(src, dst + 1024 * u);
+      const uint8_t* src = a.pool + ((uint64_t)a16[u] * 16u + g_off[u]);
+      if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(src, dst + 1024 * u);
     }
+  };
+  // steps gathered so far (score waves; wave-uniform)
+  int issued = 0;
+  // gather every step up to `upto` not yet issued
+  auto issue_upto = [&](int upto) {
+    upto = upto < nsteps - 1 ? upto : nsteps - 1;
+    for (; issued <= upto; ++issued) issue_step(issued);
   };
   // wait until this wave's rows of step k are in LDS (steps after k may still be in flight)
   auto wait_for_step = [&](int k) {
-    const int last_issued = (k - 1 + NS - 2 < nsteps - 1) ? k - 1 + NS - 2 : nsteps - 1;
-    int ahead = last_issued - k;
-    ahead = ahead < 0 ? 0 : ahead;
-    wait_steps<NL>(ahead);
+    const int ahead = issued - 1 - k;
+    if (ahead == NS - 3) {  // the steady state: every step up to k + NS - 3 issued
+      wait_steps<NL>(NS - 3);
+    } else {
+      wait_steps<NL>(ahead < 0 ? 0 : ahead);
+    }
   };
 
   // a split's normalized result tile, [NH][kTileStride] fp32, reuses the ring after the main loop
@@ -292,6 +314,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   if (scorer) {
     // ================= score waves: S^T = K q^T, P = 2^(s - ref) for rows 16rt..16rt+15 of step k
+    // The first kPrologueSteps steps (at most NS-2) are gathered before step 0 is awaited; the rest of the prefetch
+    // window follows once step 0 has landed.  With every workgroup of the launch gathering at once, a
+    // deeper first window makes the memory system interleave the steps, so that step 0 completes only
+    // when nearly all of them have.  The query staging slots (NS-2, NS-1) are not touched before every
+    // score wave holds its fragments.
+    constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
+    issue_upto(kFirst - 1);
     // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
     // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
     f16x8 qf[HT][18];
@@ -309,6 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
       }
+    wait_for_step(0);
     lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
     const int rt = r4;
     float lsum[HT];
@@ -316,8 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int tt = 0; tt < HT; ++tt) lsum[tt] = 0.0f;
 
     for (int k = 0; k <= nsteps; ++k) {
-      float sv[HT][4];
-      float psum[HT];  // sum of this lane's speculative P per head tile
+      issue_upto(k + NS - 2);  // up to the slot of step k-2 (fully consumed)
+      float sv[HT][4];  // raw scores (before the softmax scale); masked rows -inf
+      float psum[HT];   // sum of this lane's speculative P per head tile
       if (k < nsteps) {
         const uint8_t* rr = slot_ptr(k) + (16 * rt + n) * RS;
         f32x4 acc[HT];
@@ -361,47 +392,67 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             for (int tt = 0; tt < HT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][16 + ks], acc[tt]);
           }
         }
-        // scores (base 2) of rows 16rt+4g+i, heads 16tt+n; maxima; speculative P with the current ref
+        // scores of rows 16rt+4g+i, heads 16tt+n; base-2 maxima; speculative P = 2^(scale*s - ref) with
+        // the current ref.  Only the last step can hold rows past the list (its padding): masked -inf.
+        const float sl2 = a.scale_log2;
         const int rbase = k * kStepRows + 16 * rt + 4 * g;
+        const bool full = (k + 1) * kStepRows <= n_valid;
         bool raise = false;
+        float mxs[HT];
+#pragma unroll
+        for (int tt = 0; tt < HT; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[tt][i] = acc[tt][i];
+        if (!full) {
+#pragma unroll
+          for (int tt = 0; tt < HT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (rbase + i >= n_valid) sv[tt][i] = -INFINITY;
+        }
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = acc[tt][i] * a.scale_log2;
-            sv[tt][i] = rbase + i < n_valid ? x : -INFINITY;
-            mx = fmaxf(mx, sv[tt][i]);
-          }
-          raise |= mx > ref[tt] + kLazyRescale;
-          mx = group4_max(mx);
-          if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = mx;
+          mxs[tt] = max4(sv[tt][0], sv[tt][1], sv[tt][2], sv[tt][3]) * sl2;
+          raise |= mxs[tt] > ref[tt] + kLazyRescale;
           const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][i], sl2, -mr));
           psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
           write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
         }
-        if (__any(raise) && lane == 0) sh.flag[k & 1] = 1;
+        if (__any(raise)) {  // rare: publish this wave's per-head maxima and raise the flag
+#pragma unroll
+          for (int tt = 0; tt < HT; ++tt) {
+            const float mx = group4_max(mxs[tt]);
+            if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = mx;
+          }
+          if (lane == 0) sh.flag[k & 1] = 1;
+        }
       }
-      lds_barrier();  // step k's P and flag, step k+1's rows (gathered by the accumulate waves) visible
+      wait_for_step(k + 1);  // this wave's rows of step k+1 have landed
+      lds_barrier();  // step k's P, flag and maxima, step k+1's rows visible
       if (k < nsteps) {
         if (sh.flag[k & 1]) {  // rare: the reference rises; every wave takes this branch
           float alpha[HT];
           raise_reference<HT, NH>(sh.smax[k & 1], n, ref, alpha);
+          const float sl2 = a.scale_log2;
 #pragma unroll
           for (int tt = 0; tt < HT; ++tt) {
             lsum[tt] *= alpha[tt];
             const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][i], sl2, -mr));
             psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
             write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
           }
-          lds_barrier();  // rewritten P visible; every wave has read the flag
+          lds_barrier();  // rewritten P visible; every wave has read the flag and the maxima
+          // the maxima buffer of this parity starts over at -inf for its next use (step k+2)
           if (tid == 0) sh.flag[k & 1] = 0;
+#pragma unroll
+          for (int tt = 0; tt < HT; ++tt)
+            if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = -INFINITY;
         }
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt) lsum[tt] += psum[tt];
@@ -417,15 +468,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
-  // The prefetch window below the query staging slots is issued at once, so the first memory round
-  // trip of the gathers brings NS-2 steps rather than one; only step 0 is awaited before the barrier.
-  {
-#pragma unroll
-    for (int k = 0; k < NS - 2; ++k)
-      if (k < nsteps) issue_step(k);
-    const int inflight = (nsteps < NS - 2 ? nsteps : NS - 2) - 1;
-    wait_steps<NL>(inflight > 0 ? inflight : 0);
-  }
   lds_barrier();  // step 0 visible; the score waves hold their query fragments
   const int cq = r4;
   f32x4 o[HT][8];  // O^T tile c: O[head 16t+n][column 128cq+32g+8i+c] = o[t][c][i]
@@ -439,7 +481,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const uint32_t vsel = (uint32_t)((n >> 1) & 3) | ((uint32_t)(4 + ((n >> 1) & 3)) << 8);
 
   for (int k = 0; k <= nsteps; ++k) {
-    if (k + NS - 2 < nsteps) issue_step(k + NS - 2);  // into the slot of step k-2 (fully consumed)
     if (k >= 1) {
       const uint8_t* slot = slot_ptr(k - 1);
       const uint8_t* pt = sh.ptile[(k - 1) & 1];
@@ -528,7 +569,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-    wait_for_step(k + 1);  // this wave's rows of step k+1 have landed
     lds_barrier();  // matches the score waves' barrier of step k
     if (k < nsteps && sh.flag[k & 1]) {
       float alpha[HT];

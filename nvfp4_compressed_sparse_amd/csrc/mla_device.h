@@ -159,6 +159,14 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups), with the gfx950 lane
 // swaps (VALU, no LDS round trip): swap(x, x) yields the pair {x[l], x[l^32]} (resp. x[l^16]).
+// Largest of four floats (no NaN among the inputs: matrix-core results or -inf), as two v_max3_f32
+// without the quieting steps the compiler adds to fmaxf on values it cannot prove canonical.
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return r;
+}
+
 __device__ __forceinline__ float group4_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -64,6 +64,9 @@ def test_sparse_decode_argument_errors():
     assert _sparse(q=FAKE + 8) == 3
     assert _sparse(out=FAKE + 2) == 3
     assert _sparse(sc=float("nan")) == 2
+    assert _sparse(sc=0.0) == 2
+    assert _sparse(sc=-0.07) == 2
+    assert _sparse(sc=float("inf")) == 2
     # split path needs a workspace of the advertised size
     need = M.lib().mla_sparse_decode_workspace_bytes(2, 1, 16, 256, 4)
     assert need > 0
