@@ -52,6 +52,7 @@ constexpr float kLazyRescale = 8.0f;   // log2 headroom of the lazy softmax refe
 constexpr int kPStride = kStepRows * 2 + 16;  // bytes per head of a P tile: 64 FP16 values + padding
 constexpr int kTileStride = kLatent + 4;       // floats per head of a split's result tile in LDS (padded)
 constexpr int kPrologueSteps = 3;              // steps gathered before step 0 is awaited
+constexpr int kHeadStart = 2;                  // of those, steps gathered before the query fragments
 
 // Geometry of the raw-row ring: steps of 64 rows; each of the four score waves gathers 16 rows of each
 // step (the accumulate waves have the longer instruction stream per step, so the score waves, which
@@ -314,13 +315,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   if (scorer) {
     // ================= score waves: S^T = K q^T, P = 2^(s - ref) for rows 16rt..16rt+15 of step k
-    // The first kPrologueSteps steps (at most NS-2) are gathered before step 0 is awaited; the rest of the prefetch
+    // The first kPrologueSteps steps (at most NS-2) are gathered before step 0 is awaited, kHeadStart of
+    // them before the query fragments are formed and the rest after; the remainder of the prefetch
     // window follows once step 0 has landed.  With every workgroup of the launch gathering at once, a
     // deeper first window makes the memory system interleave the steps, so that step 0 completes only
-    // when nearly all of them have.  The query staging slots (NS-2, NS-1) are not touched before every
-    // score wave holds its fragments.
+    // when nearly all of them have; the staggered issue lets the first steps' requests queue first.
+    // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
     constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
-    issue_upto(kFirst - 1);
+    constexpr int kEarly = kHeadStart < kFirst ? kHeadStart : kFirst;
+    issue_upto(kEarly - 1);
     // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
     // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
     f16x8 qf[HT][18];
@@ -338,6 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
       }
+    issue_upto(kFirst - 1);
     wait_for_step(0);
     lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
     const int rt = r4;
