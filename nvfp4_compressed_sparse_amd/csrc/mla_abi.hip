@@ -135,6 +135,8 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   int S = num_splits;
   int chunk = (int)ceil_div(entries, S);
+  // a dense split starts on a page boundary, so that each 64-row step of the decoder is one page
+  if (!indices) chunk = (int)ceil_div(chunk, 64) * 64;
   if (chunk > kMaxChunk) return MLA_ERR_SHAPE;
   size_t need = workspace_for(B, T, H, S);
   if (need > 0) {

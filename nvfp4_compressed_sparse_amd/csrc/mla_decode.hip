@@ -16,7 +16,7 @@
 //     are validated (index < 0, past the causal limit, or on a page-table entry outside the pool ->
 //     dropped, which also skips their loads) and compacted into an LDS list of row addresses (order
 //     kept, so results are deterministic).
-//   * rows are consumed in steps of 64; the score waves gather them by LDS-DMA (16 bytes per lane, no
+//   * rows are consumed in steps of 64; one role's waves gather them by LDS-DMA (16 bytes per lane, no
 //     registers) into a ring of raw row slots, several steps ahead.
 //   * the waves specialise, as the pages' warp groups do: waves 0-3 score, waves 4-7 accumulate, one of
 //     each per SIMD, so each SIMD interleaves a scoring and an accumulating wave.  The two roles work one
@@ -55,8 +55,7 @@ constexpr int kPrologueSteps = 3;              // steps gathered before step 0 i
 constexpr int kHeadStart = 2;                  // of those, steps gathered before the query fragments
 
 // Geometry of the raw-row ring: steps of 64 rows; each of the four score waves gathers 16 rows of each
-// step (the accumulate waves have the longer instruction stream per step, so the score waves, which
-// would otherwise wait at the step barrier, take the gathers).  In LDS a row
+// step (see the kernel for why the score waves).  In LDS a row
 // takes one 16-byte chunk more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes
 // of a lane group start on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l
 // of a wave's DMA load u fills LDS chunk 64u+l of the wave's 16 rows; the padding chunks are not
@@ -71,7 +70,7 @@ struct Geo {
   static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 6 or 10 DMA loads per wave per step
   static_assert((kLoads - 1) * 64 < kWaveChunks, "only a wave's last gather load is partial");
   static constexpr int kSlot = kStepRows * kStride;              // bytes of one step
-  static constexpr int kSlots = FMT == 0 ? 6 : 3;                // ring depth
+  static constexpr int kSlots = FMT == 0 ? 6 : 4;                // ring depth
   static constexpr int kRing = kSlots * kSlot;
 };
 
@@ -88,12 +87,14 @@ __device__ __forceinline__ void write_p(uint8_t* prow, int rt, int g, const floa
   *reinterpret_cast<f16x2*>(prow + 2 * (32 + 8 * g + 2 * rt)) = p23;
 }
 
-// LDS state shared by the roles.
-template <int FMT, int NH>
+// LDS state shared by the roles.  A sparse list keeps the 16-byte addresses of its valid rows; a dense
+// split (64-aligned, so that each step is one page) keeps its page-table entries instead.
+template <int FMT, int NH, bool DENSE>
 struct Shared {
   uint8_t ring[Geo<FMT>::kRing];
-  uint8_t ptile[2][NH * kPStride];  // P of steps k (even/odd): [head][row], FP16
-  uint32_t rowlist[kMaxChunk];      // 16-byte row addresses of the split's valid entries
+  uint8_t ptile[2][NH * kPStride];             // P of steps k (even/odd): [head][row], FP16
+  uint32_t rowlist[DENSE ? 1 : kMaxChunk];     // sparse: row addresses of the split's valid entries
+  int pages[DENSE ? kMaxChunk / kStepRows : 1];  // dense: page of each step, -1 = not in the pool
   float smax[2][NH][4];             // per-score-wave maxima of step k, per head
   float wsum[NH][4];                // per-score-wave softmax sums
   int flag[2];                      // step k raised the softmax reference
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int NL = G::kLoads;
   constexpr int NS = G::kSlots;
   constexpr int NH = 16 * HT;
-  __shared__ __attribute__((aligned(16))) Shared<FMT, NH> sh;
+  __shared__ __attribute__((aligned(16))) Shared<FMT, NH, DENSE> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,20 +159,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- prologue: valid rows of this split -> LDS list of 16-byte row addresses.
-  // The page-table entries this split can touch (the request's whole table row for a sparse list, the
-  // pages of the split's position range for a dense one; neither depends on the context length) are
-  // staged in LDS with coalesced loads while the context length and the split's list entries load at
-  // the same time: one memory round trip instead of two or three dependent ones.
   const int e0 = s * a.chunk;
-  const int p0 = DENSE ? (e0 >> 6) : 0;
-  int npg = DENSE ? (int)(((int64_t)e0 + a.chunk - 1) / 64 - p0 + 1) : (int)a.bt_stride;
-  if (p0 + npg > a.bt_stride) npg = (int)a.bt_stride - p0;
-  if (npg < 0) npg = 0;
+  const int* btg = a.block_table + (int64_t)b * a.bt_stride;
+  const int L = a.ctx[b];
+  const int lim = a.causal ? L - a.T + t : L - 1;
+  if (tid < 2) sh.flag[tid] = 0;
+  // published maxima start at -inf: a raise takes the largest published value, and only waves that
+  // raise publish (every score a wave saw before stays within 2^8 of the reference it left behind)
+  if (tid < 2 * NH * 4) (&sh.smax[0][0][0])[tid] = -INFINITY;
+  int n_valid;
+  if constexpr (DENSE) {
+    // ---- prologue, dense: the split covers positions [e0, e1), e0 a multiple of 64 (the chunk is), so
+    // step k is the request's logical page (e0 >> 6) + k; its table entry is staged, -1 when it is not
+    // in the pool or lies beyond the table width (those rows select nothing: their scores are masked)
+    const int e_end = lim + 1 < a.entries ? lim + 1 : a.entries;
+    const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
+    n_valid = e1 > e0 ? e1 - e0 : 0;
+    if (tid < a.chunk / kStepRows) {
+      const int p = (e0 >> 6) + tid;
+      const int pg = p < a.bt_stride ? btg[p] : -1;
+      sh.pages[tid] = pg >= 0 && pg < a.num_pages ? pg : -1;
+    }
+    wait_vmem();      // the query DMA has landed
+    __syncthreads();  // staged pages and queries visible
+  } else {
+  // ---- prologue, sparse: valid rows of this split -> LDS list of 16-byte row addresses.
+  // The request's whole page-table row (it does not depend on the context length) is staged in LDS
+  // with coalesced loads while the context length and the split's list entries load at the same
+  // time: one memory round trip instead of two or three dependent ones.
+  const int npg = (int)a.bt_stride;
   constexpr int kBtCap = (NS - 2) * G::kSlot / 4;  // below the query staging area
   const bool staged = npg <= kBtCap;
   int* btl = reinterpret_cast<int*>(sh.ring);
-  const int* btg = a.block_table + (int64_t)b * a.bt_stride + p0;
   constexpr int kBtPer = 6;  // entries per thread loaded before any is stored (tables up to 3,072 pages)
   const bool bt_regs = npg <= kThreads * kBtPer;
   int btv[kBtPer];
@@ -179,10 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kBtPer; ++k) btv[k] = tid + kThreads * k < npg ? btg[tid + kThreads * k] : 0;
   }
-  const int L = a.ctx[b];
-  const int lim = a.causal ? L - a.T + t : L - 1;
-  const int e_end = DENSE ? (lim + 1 < a.entries ? lim + 1 : a.entries) : a.entries;
-  const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
+  const int e1 = (e0 + a.chunk < a.entries) ? e0 + a.chunk : a.entries;
 
   constexpr int EPT = kEntriesPerThread;
   int pos[EPT];
@@ -190,19 +206,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   for (int k = 0; k < EPT; ++k) pos[k] = -1;
   if (e1 > e0) {
     const int ebase = e0 + EPT * tid;
-    if (DENSE) {
+    const int* ip = a.indices + (int64_t)qtok * a.entries + ebase;
+    if (((uintptr_t)a.indices & 15) == 0 && (((int64_t)qtok * a.entries + e0) & 3) == 0 && ebase + EPT <= e1) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(ip);
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ebase + k : -1;
+      for (int k = 0; k < 4; ++k) pos[k] = (int)x0[k];
     } else {
-      const int* ip = a.indices + (int64_t)qtok * a.entries + ebase;
-      if (((uintptr_t)a.indices & 15) == 0 && (((int64_t)qtok * a.entries + e0) & 3) == 0 && ebase + EPT <= e1) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(ip);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pos[k] = (int)x0[k];
-      } else {
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
-      }
+      for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
     }
   }
   if (bt_regs) {
@@ -212,10 +223,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   } else if (staged) {
     for (int i = tid; i < npg; i += kThreads) btl[i] = btg[i];
   }
-  if (tid < 2) sh.flag[tid] = 0;
-  // published maxima start at -inf: a raise takes the largest published value, and only waves that
-  // raise publish (every score a wave saw before stays within 2^8 of the reference it left behind)
-  if (tid < 2 * NH * 4) (&sh.smax[0][0][0])[tid] = -INFINITY;
   __syncthreads();  // staged page-table entries visible
 
   uint32_t addr[EPT];
@@ -225,9 +232,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int pg = (pos[k] >= 0 ? pos[k] : 0) >> 6;
     // a position past the limit, or on a page beyond the table width (only with a context longer than
     // the table allows), selects nothing
-    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg - p0 < npg;
+    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg < npg;
     int page = -1;
-    if (inr) page = staged ? btl[pg - p0] : btg[pg - p0];
+    if (inr) page = staged ? btl[pg] : btg[pg];
     const bool ok = inr && page >= 0 && page < a.num_pages;
     addr[k] = ok ? (uint32_t)(((uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(pos[k] & 63) * ROWB) >> 4) : 0u;
     vmask |= (uint32_t)ok << k;
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   }
   if (lane == 0) sh.wcount[w] = wave_total;
   __syncthreads();
-  int n_valid = 0;
+  n_valid = 0;
 #pragma unroll
   for (int ww = 0; ww < kWaves; ++ww) {
     off += ww < w ? sh.wcount[ww] : 0;
@@ -259,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // every load issued so far (indices, page table, the query DMA) has landed before the gathers start
   wait_vmem();
   __syncthreads();  // row list and staged queries complete; the page-table staging area is free again
+  }
 
   const int nsteps = (n_valid + kStepRows - 1) / kStepRows;
   auto slot_ptr = [&](int st) { return sh.ring + (st % NS) * G::kSlot; };
@@ -266,6 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // + 1).  The chunk after a row's last one is the row's padding: it receives the row's first chunk
   // again, so that only the lanes past the wave's last row (in its last load) are masked.  Per lane and
   // load: the row within the wave's rows and the byte offset of the chunk.
+  // (dense: the byte offset within the step's page of that row and chunk)
   int g_row[NL];
   uint32_t g_off[NL];
 #pragma unroll
@@ -274,20 +283,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int c = e % (G::kChunks + 1);
     g_row[u] = e / (G::kChunks + 1);
     g_off[u] = c < G::kChunks ? 16u * c : 0u;
+    if (DENSE) g_off[u] += (uint32_t)((G::kWaveRows * r4 + g_row[u]) * ROWB);
   }
-  auto issue_step = [&](int st) {  // score waves only
-    const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
+  auto issue_step = [&](int st) {  // the gathering role only
     const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
-    // every row address is read first (one LDS round trip), then the loads go out
-    uint32_t a16[NL];
+    if constexpr (DENSE) {
+      // one page per step (a page outside the pool reads the pool's first page; its rows are masked)
+      const int pg = __builtin_amdgcn_readfirstlane(sh.pages[st]);
+      const uint8_t* base = a.pool + (pg >= 0 ? (uint64_t)pg * (uint64_t)a.page_stride : 0ull);
 #pragma unroll
-    for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
+      for (int u = 0; u < NL; ++u)
+        if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(base + g_off[u], dst + 1024 * u);
+    } else {
+      const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
+      // every row address is read first (one LDS round trip), then the loads go out
+      uint32_t a16[NL];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const uint8_t* src = a.pool + ((uint64_t)a16[u] * 16u + g_off[u]);
-      if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(src, dst + 1024 * u);
+      for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint8_t* src = a.pool + ((uint64_t)a16[u] * 16u + g_off[u]);
+        if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(src, dst + 1024 * u);
+      }
     }
   };
+  // The score waves gather.  Issuing a step's LDS-DMA loads stalls the issuing wave for a while (the
+  // vector memory path takes them at a limited rate); with NVFP4 rows the accumulate waves have the
+  // longer instruction stream (dequantizing V costs more than K's share), so the score waves, which
+  // would otherwise wait at the step barrier, absorb it.  (FP8 rows leave the score waves no such
+  // slack, but neither the accumulate waves nor all eight waves together issue them faster.)
+  constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
+  constexpr int kEarly = kHeadStart < kFirst ? kHeadStart : kFirst;
   // steps gathered so far (score waves; wave-uniform)
   int issued = 0;
   // gather every step up to `upto` not yet issued
@@ -321,8 +347,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // deeper first window makes the memory system interleave the steps, so that step 0 completes only
     // when nearly all of them have; the staggered issue lets the first steps' requests queue first.
     // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
-    constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
-    constexpr int kEarly = kHeadStart < kFirst ? kHeadStart : kFirst;
     issue_upto(kEarly - 1);
     // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
     // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
@@ -400,7 +424,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         // the current ref.  Only the last step can hold rows past the list (its padding): masked -inf.
         const float sl2 = a.scale_log2;
         const int rbase = k * kStepRows + 16 * rt + 4 * g;
-        const bool full = (k + 1) * kStepRows <= n_valid;
+        // (dense: a step whose page is not in the pool selects nothing)
+        const bool page_ok = !DENSE || sh.pages[DENSE ? k : 0] >= 0;
+        const bool full = (k + 1) * kStepRows <= n_valid && page_ok;
         bool raise = false;
         float mxs[HT];
 #pragma unroll
@@ -412,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
           for (int tt = 0; tt < HT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (rbase + i >= n_valid) sv[tt][i] = -INFINITY;
+              if (rbase + i >= n_valid || !page_ok) sv[tt][i] = -INFINITY;
         }
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt) {

@@ -311,6 +311,25 @@ def test_dense_fp8_decode(T, causal, S):
     say(compare_outputs(out, ro, lse, rl, f"dense T={T} S={S}"))
 
 
+def test_dense_fp8_pages_outside_the_pool():
+    """Page-table entries outside [0, num_pages) select nothing: in the middle of a context, on its
+    last (partial) page, and for a split that holds only such pages."""
+    cfg = small(B=3, T=1, H=128, topk=0, fmt="fp8", L=1500, seed=41)
+    case = Case(cfg, ctx=[1500, 900, 70])
+    bt = case.lay.block_table
+    bt[0, 2] = -1
+    bt[0, 5] = case.lay.num_pages + 3
+    bt[1, 14] = -2  # request 1's last page (900 = 14 * 64 + 4)
+    bt[2, 0] = case.lay.num_pages  # request 2 keeps only positions 64..69
+    say("dense fp8 pages outside the pool")
+    d = case.to_device()
+    gpu_pool(case, d)
+    for S in (1, 3, 0):
+        out, lse = gpu_decode(case, d, num_splits=S)
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(out, ro, lse, rl, f"dense invalid pages S={S}"))
+
+
 # --------------------------------------------------------------------------- full-size configs, sampled
 def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
     """Oracle results for sampled query tokens of a full-size device case: the selected source rows are
