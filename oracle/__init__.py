@@ -63,6 +63,7 @@ def _load():
         "mlo_sparse_decode": (i32, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, d, i32, P, i64, P, P, i32]),
         "mlo_dense_decode_fp8": (i32, [P, P, i64, i64, P, i64, P, i32, i32, i32, d, i32, P, i64, P, P, i32]),
         "mlo_merge_partials": (None, [P, P, i32, i32, P, P]),
+        "mlo_stage_nvfp4_fp8": (None, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, i64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -225,3 +226,24 @@ def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
     lse = np.empty(H, np.float64)
     _load().mlo_merge_partials(_ptr(o), _ptr(l), S, H, _ptr(out), _ptr(lse))
     return out, lse
+
+
+# --------------------------------------------------------------------------- staged path
+
+def stage_nvfp4_fp8(pool, page_stride, num_pages, block_table, ctx, indices, causal=False, rows_per_token=None):
+    """The staged path (launch post, native NVFP4 sparse MLA decode section; analysis page, "A kernel
+    that reads four bits directly"): each query token's selected NVFP4 rows unpacked into 576-byte FP8
+    rows of a temporary buffer.  indices int32 [B,T,k].  Returns (staged uint8 [B*T, R, 576] with R =
+    rows_per_token (default k rounded up to whole 64-row pages), counts int32 [B*T]); row id*R + j for
+    j < counts[id] is the j-th selected row of query token id, later rows are zero."""
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    B, T, k = idx.shape
+    R = ((k + PAGE - 1) // PAGE) * PAGE if rows_per_token is None else int(rows_per_token)
+    assert R >= k
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cx = np.ascontiguousarray(ctx, dtype=np.int32)
+    staged = np.zeros((B * T, R, FP8_ROW_BYTES), np.uint8)
+    counts = np.zeros(B * T, np.int32)
+    _load().mlo_stage_nvfp4_fp8(_ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T,
+                                k, int(bool(causal)), R, _ptr(staged), _ptr(counts))
+    return staged, counts

@@ -83,7 +83,8 @@ double mlo_e2m1_value(uint32_t code) {
 /* ------------------------------------------------------------------ encoders (nearest value) */
 
 /* Code (0..126) of the non-negative finite E4M3FN value nearest to num/den, ties to the even
- * code.  num >= 0, den > 0, num a bf16 value, den in {1, 6}.  Brute force over every candidate. */
+ * code.  num >= 0, den > 0, num a bf16 value or a product e2m1 x E4M3 (at most 6 significant bits),
+ * den in {1, 6}.  Brute force over every candidate. */
 static uint32_t nearest_e4m3_code(double num, double den) {
   if (num >= 448.0 * den) return 0x7E;               /* nothing finite lies above 448 */
   if (num <= ldexp(den, -10)) return 0;              /* at most half the smallest step: 0 (tie -> even 0) */
@@ -338,6 +339,44 @@ int mlo_dense_decode_fp8(const uint16_t* q, const uint8_t* pool, int64_t page_st
     free(z);
   }
   return used;
+}
+
+/* ------------------------------------------------------------------ staged path */
+
+/* The staged path the launch post used first (section "原生 NVFP4 稀疏 MLA 解码内核"; analysis
+ * page, section "A kernel that reads four bits directly", staged-versus-native figure): the rows a
+ * query token selects are unpacked from NVFP4 into 576-byte FP8 rows of a temporary buffer, and an FP8
+ * attention kernel reads that copy.  Query token id = b*T + t gets its selected rows (the sparse
+ * decode's selection, in list order) at staged rows id*rows_per_token + 0..n-1, and counts[id] = n.
+ * Latent value d of a row is the exact product e2m1 x block scale, cast to E4M3 (nearest finite, ties
+ * to the even code, saturating at 448; sign = nibble sign xor scale sign); the 64 rope bytes are copied.
+ * Staged rows past n are left as they were.  Scale bytes 0x7F/0xFF (NaN) never come from the writer;
+ * their output is not defined here. */
+void mlo_stage_nvfp4_fp8(const uint8_t* pool, int64_t page_stride, int64_t num_pages, const int32_t* block_table,
+                         int64_t bt_stride, const int32_t* ctx, const int32_t* indices, int B, int T, int topk,
+                         int causal, int64_t rows_per_token, uint8_t* staged, int32_t* counts) {
+  for (int64_t id = 0; id < (int64_t)B * T; ++id) {
+    int b = (int)(id / T), t = (int)(id % T);
+    int64_t lim = position_limit(ctx[b], T, t, causal);
+    const int32_t* idx = indices + id * topk;
+    int32_t n = 0;
+    for (int j = 0; j < topk; ++j) {
+      const uint8_t* row = row_address(pool, page_stride, num_pages, NVFP4_ROW, block_table, bt_stride, b, idx[j], lim);
+      if (!row) continue;
+      uint8_t* dst = staged + (id * rows_per_token + n) * FP8_ROW;
+      for (int d = 0; d < LATENT; ++d) {
+        uint32_t byte = row[d / 2];
+        uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 15);
+        uint32_t sc = row[256 + d / 16];
+        double mag = fabs(mlo_e2m1_value(nib)) * fabs(mlo_e4m3_value(sc));
+        uint32_t sign = ((nib >> 3) ^ (sc >> 7)) & 1;
+        dst[d] = (uint8_t)((sign << 7) | nearest_e4m3_code(mag, 1.0));
+      }
+      memcpy(dst + LATENT, row + 288, ROPE);
+      ++n;
+    }
+    counts[id] = n;
+  }
 }
 
 /* Merge S partial results of one query token computed over disjoint parts of its selection:

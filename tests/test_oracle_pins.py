@@ -498,3 +498,96 @@ def test_units_subset_matches_full_run():
     units = np.array([5, 0, 3], np.int64)
     out_u, lse_u, _ = oracle.sparse_decode(q, pool, *args, idx, cfg.sm_scale, causal=True, units=units)
     assert np.array_equal(out_u, out[units]) and np.array_equal(lse_u, lse[units])
+
+
+# --------------------------------------------------------------------------- staged path (NVFP4 -> FP8 copy)
+def _all_pairs_pool():
+    """One page whose rows hold every (scale byte, nibble) pair: block j of row r has scale code
+    sc = 32r + j (NaN codes 0x7F / 0xFF replaced by 0) and nibbles 0..15."""
+    rows = []
+    for r in range(8):
+        row = np.zeros(352, np.uint8)
+        for j in range(32):
+            sc = 32 * r + j
+            row[256 + j] = 0 if sc in (0x7F, 0xFF) else sc
+            nib = np.arange(16, dtype=np.uint8)
+            row[8 * j:8 * j + 8] = nib[0::2] | (nib[1::2] << 4)
+        row[288:352] = np.arange(64, dtype=np.uint8) * 3 + r
+        rows.append(row)
+    pool = np.zeros(64 * 352, np.uint8)
+    pool[:8 * 352] = np.concatenate(rows)
+    return pool, rows
+
+
+def test_stage_fp8_every_scale_and_nibble_vs_torch_cast():
+    """Each staged latent byte is the E4M3 cast of the exact product e2m1 x scale: torch's float8_e4m3fn
+    cast (nearest, ties to even) below 448, 448 with the product's sign at or above it."""
+    pool, rows = _all_pairs_pool()
+    idx = np.arange(8, dtype=np.int32).reshape(1, 1, 8)
+    staged, counts = oracle.stage_nvfp4_fp8(pool, 64 * 352, 1, np.zeros((1, 1), np.int32), np.array([8], np.int32), idx)
+    assert counts.tolist() == [8]
+    checked = 0
+    for r, row in enumerate(rows):
+        got = staged[0, r, :512].astype(np.int64)
+        for d in range(512):
+            nib = (row[d // 2] >> (4 * (d & 1))) & 15
+            sc = int(row[256 + d // 16])
+            prod = minifloat(int(nib), 2, 1, 1) * minifloat(sc, 4, 3, 7)  # exact in double
+            neg = bool(nib >> 3) != bool(sc >> 7)
+            if abs(prod) < 448.0:
+                ref = int(torch.tensor([prod], dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+                # a zero product keeps the sign rule (nibble sign xor scale sign) where the cast of +-0 does not
+                if prod == 0.0:
+                    ref = 0x80 if neg else 0x00
+            else:
+                ref = 0x7E | (0x80 if neg else 0)
+            assert got[d] == ref, (r, d, nib, sc, prod, got[d], ref)
+            checked += 1
+        assert np.array_equal(staged[0, r, 512:], row[288:352])  # rope bytes copied
+    assert checked == 8 * 512
+
+
+def test_stage_fp8_selection_order_and_counts():
+    """The staged rows are the sparse decode's selection in list order (invalid entries skipped), and
+    their dequantized values are the NVFP4 values rounded to E4M3 (within half an E4M3 step)."""
+    cfg, lay, pool, q, idx, rng = _small_case(31, B=3, T=2, L=700, topk=128, causal=True)
+    idx = idx.copy()
+    idx[0, 0, :20] = -1
+    idx[1, 1, 5:9] = 10 ** 6
+    lay.block_table[2, 3] = lay.num_pages + 1
+    staged, counts = oracle.stage_nvfp4_fp8(pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, idx,
+                                            causal=True)
+    assert staged.shape == (6, 128, 576)
+    for b in range(3):
+        for t in range(2):
+            lim = W.position_limit(int(lay.ctx[b]), 2, t, True)
+            sel = [p for p in idx[b, t] if 0 <= p <= lim and 0 <= lay.block_table[b, p // 64] < lay.num_pages]
+            n = counts[b * 2 + t]
+            assert n == len(sel)
+            for j, p in enumerate(sel):
+                src = _rows_of(cfg, lay, pool, b, [p])[0]
+                K = _independent_K(src, "nvfp4")
+                got = _independent_K(staged[b * 2 + t, j], "fp8")
+                assert np.array_equal(got[512:], K[512:])
+                err = np.abs(got[:512] - K[:512])
+                assert np.all(err <= np.maximum(np.abs(K[:512]) * 2.0 ** -4, 2.0 ** -10)), (b, t, j)
+            assert not staged[b * 2 + t, n:].any()
+
+
+def test_staged_decode_close_to_native_decode():
+    """FP8 attention over the staged copy (identity page table over the copy, one query token per
+    request) approximates the native decode of the same selection: the copy only rounds values to E4M3."""
+    cfg, lay, pool, q, idx, rng = _small_case(32, B=2, T=1, H=8, L=900, topk=256)
+    staged, counts = oracle.stage_nvfp4_fp8(pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, idx)
+    nq, R = staged.shape[:2]
+    P = R // 64
+    bt = (np.arange(nq)[:, None] * P + np.arange(P)[None, :]).astype(np.int32)
+    o_st, l_st, _ = oracle.dense_decode_fp8(q.reshape(nq, 1, cfg.H, 576), staged.reshape(-1), 64 * 576, nq * P, bt,
+                                            counts, cfg.sm_scale)
+    o_na, l_na, _ = oracle.sparse_decode(q, pool, cfg.page_stride, lay.num_pages, lay.block_table, lay.ctx, idx,
+                                         cfg.sm_scale)
+    # Scores move by sm_scale * <q, K' - K> with |K' - K| <= 2^-4 |K| per value: a few hundredths
+    # typically, a few tenths at the extremes of 2,048 scores.  A lost scale or sign moves both by O(1).
+    rel = np.linalg.norm(o_st - o_na) / np.linalg.norm(o_na)
+    assert 0 < rel < 0.05, rel
+    assert np.abs(l_st - l_na).max() < 0.5
