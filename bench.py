@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sparse", choices=sorted(W.CONFIGS))
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--path", default="native", choices=["native", "staged"],
+                    help="sparse workloads: native NVFP4 decode, or the staged path (unpack the selected rows "
+                         "to an FP8 copy, then the FP8 decoder reads it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -119,6 +122,9 @@ def main():
     import nvfp4_compressed_sparse_amd as M
 
     cfg = W.CONFIGS[args.workload]
+    staged_path = args.path == "staged"
+    if staged_path and not (cfg.topk and cfg.fmt == "nvfp4"):
+        raise SystemExit("--path staged applies to the sparse NVFP4 workloads")
     dev = "cuda"
     torch.cuda.set_device(0)
     log(f"[bench] workload {cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} topk={cfg.topk} fmt={cfg.fmt}")
@@ -158,6 +164,18 @@ def main():
     lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     max_ctx = int(lay.ctx.max())
+    if staged_path:
+        # the FP8 copy of every query token's selected rows, read by the FP8 decoder as a paged cache
+        nq = cfg.B * cfg.T
+        st_pages = (cfg.topk + 63) // 64
+        staged = torch.empty(nq * st_pages * 64 * 576, dtype=torch.uint8, device=dev)
+        st_bt = torch.empty((nq, st_pages), dtype=torch.int32, device=dev)
+        st_len = torch.empty(nq, dtype=torch.int32, device=dev)
+        S = args.splits or M.mla_dense_decode_splits(nq, 1, cfg.H, st_pages * 64)
+        ws_bytes = M.mla_dense_decode_workspace_bytes(nq, 1, cfg.H, st_pages * 64, S)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        out1 = out.view(nq, 1, cfg.H, 512)
+        lse1 = lse.view(nq, 1, cfg.H)
 
     # valid selected rows per set (algorithmic work)
     if cfg.topk:
@@ -174,7 +192,14 @@ def main():
         quant(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        if cfg.topk:
+        if staged_path:
+            M.mla_stage_nvfp4_fp8(pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k],
+                                  causal=cfg.causal, staged=staged, staged_block_table=st_bt, staged_lens=st_len,
+                                  stream=stream)
+            M.mla_dense_decode_fp8(q_sets[k].view(nq, 1, cfg.H, 576), staged, 64 * 576, nq * st_pages, st_bt, st_len,
+                                   st_pages * 64, cfg.sm_scale, num_splits=S, out=out1, lse=lse1, workspace=ws,
+                                   stream=stream)
+        elif cfg.topk:
             M.mla_sparse_decode(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k],
                                 cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
                                 stream=stream)
@@ -212,6 +237,9 @@ def main():
     value = nq / (ms_per_step * 1e-3)
     vrows = float(np.mean([valid[i % N_SETS] for i in range(args.steps)]))
     bytes_per, flops_per = algorithmic_work(cfg, vrows)
+    if staged_path:
+        # the staged path moves a selected row three times: 352 B read, 576 B FP8 copy written and read
+        bytes_per += int(vrows * 2 * 576)
     if cfg.H <= 32:
         ach = bytes_per / (dec_avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -220,13 +248,17 @@ def main():
         ach = flops_per / (dec_avg_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-    t = profile_record(cfg, "traffic", "traffic_bytes_per_launch")
+    t = None if staged_path else profile_record(cfg, "traffic", "traffic_bytes_per_launch")
     roof["traffic"] = None if t is None else int(t)
     if cfg.H > 32:
         roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent")
-    roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + " call: " + \
-        ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
-        " (split merge inside), timed with HIP events on its stream"
+    if staged_path:
+        roof["kernel"] = ("mla_stage_nvfp4_fp8 + mla_dense_decode_fp8 calls: stage_rows_kernel then decode_kernel "
+                          "over the FP8 copy, timed together with HIP events on their stream")
+    else:
+        roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + " call: " + \
+            ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
+            " (split merge inside), timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)
@@ -246,8 +278,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "H": cfg.H, "topk": cfg.topk,
                    "context": cfg.ctx or list(cfg.ctx_range), "row_bytes": cfg.row_bytes, "page_tokens": 64,
-                   "causal": cfg.causal, "splits": S, "step": ("quantize %d rows + decode" %
-                                                               (cfg.quant_chunk or nq))},
+                   "causal": cfg.causal, "splits": S, "path": args.path,
+                   "step": ("quantize %d rows + %s" % (cfg.quant_chunk or nq,
+                                                       "stage + FP8 decode" if staged_path else "decode"))},
         "roofline": roof,
         "cpu_baseline": None,
     }

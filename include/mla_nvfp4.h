@@ -157,6 +157,30 @@ int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_by
                          int32_t num_splits, void* out, float* lse, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * The staged path, for comparison (launch post, native NVFP4 sparse MLA decode section; the analysis
+ * page, "A kernel that reads four bits directly": before the native kernel, the selected rows were
+ * unpacked into a temporary FP8 buffer that an FP8 attention kernel then read, 352 + 576 + 576 bytes per
+ * row).  For every query token id = b*T + t, the rows mla_sparse_decode would select (same rule, list
+ * order) are unpacked into 576-byte FP8 rows: latent value = e2m1 x block scale (exact) cast to E4M3
+ * (nearest, ties to even, saturating at 448, sign = nibble sign xor scale sign), rope bytes copied.
+ * The copy is a paged FP8 cache of B*T*P pages (P = ceil(topk/64)) that mla_dense_decode_fp8 reads with
+ * q viewed as [B*T, 1, H, 576], page stride 64*576, num_pages B*T*P, this call's block table (bt_stride
+ * P), context_lens = staged_lens, max_context P*64 and causal 0: the causal limit is already applied.
+ *   pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, topk, causal:
+ *                      as for mla_sparse_decode
+ *   staged             (device) B*T*P*64*576 bytes, 16-byte aligned: query token id's j-th selected row
+ *                      at byte ((id*P*64) + j) * 576; rows past its count are not written
+ *   staged_block_table (device) int32 [B*T, P], written: entry id*P + p
+ *   staged_lens        (device) int32 [B*T], written: the number of rows staged for query token id
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (sizes as for mla_sparse_decode), MLA_ERR_STRIDE_ALIGN,
+ * MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num_pages, const int32_t* block_table,
+                        int64_t bt_stride, const int32_t* context_lens, const int32_t* indices, int32_t B, int32_t T,
+                        int32_t topk, int32_t causal, void* staged, int32_t* staged_block_table, int32_t* staged_lens,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

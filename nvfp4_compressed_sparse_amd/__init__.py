@@ -23,7 +23,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_dense_decode_fp8",
+    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8",
 ]
 
 
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
                                              sz, P]),
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
+        "mla_stage_nvfp4_fp8": (ctypes.c_int, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -211,3 +212,37 @@ def mla_dense_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, con
                                     0 if workspace is None else workspace.numel(), _stream(stream))
     _check("mla_dense_decode_fp8", st)
     return out, lse
+
+
+def mla_stage_nvfp4_fp8(pool, page_stride_bytes, num_pages, block_table, context_lens, indices, causal=False,
+                        staged=None, staged_block_table=None, staged_lens=None, stream=None):
+    """The staged path's unpack: each query token's selected NVFP4 rows as 576-byte FP8 rows of a paged
+    copy.  Returns (staged uint8 [B*T*P*64*576], staged_block_table int32 [B*T, P], staged_lens int32
+    [B*T]), P = ceil(topk/64); mla_dense_decode_fp8 reads the copy (see include/mla_nvfp4.h)."""
+    import torch
+    _dev(pool, torch.uint8, "pool")
+    _dev(indices, torch.int32, "indices")
+    if indices.dim() != 3 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [B, T, topk] int32 tensor")
+    B, T, topk = indices.shape
+    if block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != B:
+        raise ValueError("block_table must be a contiguous [B, pages] int32 tensor")
+    if context_lens.numel() != B or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+    P = (topk + PAGE_TOKENS - 1) // PAGE_TOKENS
+    dev = indices.device
+    if staged is None:
+        staged = torch.empty(B * T * P * PAGE_TOKENS * FP8_ROW_BYTES, dtype=torch.uint8, device=dev)
+    if staged_block_table is None:
+        staged_block_table = torch.empty((B * T, P), dtype=torch.int32, device=dev)
+    if staged_lens is None:
+        staged_lens = torch.empty(B * T, dtype=torch.int32, device=dev)
+    if staged.numel() < B * T * P * PAGE_TOKENS * FP8_ROW_BYTES or tuple(staged_block_table.shape) != (B * T, P) \
+            or staged_lens.numel() != B * T:
+        raise ValueError("staged buffers have the wrong size")
+    st = lib().mla_stage_nvfp4_fp8(pool.data_ptr(), int(page_stride_bytes), int(num_pages), block_table.data_ptr(),
+                                   block_table.stride(0), context_lens.data_ptr(), indices.data_ptr(), B, T, topk,
+                                   int(bool(causal)), staged.data_ptr(), staged_block_table.data_ptr(),
+                                   staged_lens.data_ptr(), _stream(stream))
+    _check("mla_stage_nvfp4_fp8", st)
+    return staged, staged_block_table, staged_lens

@@ -1,5 +1,6 @@
 // C ABI of libmla_nvfp4 (declared in include/mla_nvfp4.h): host-side argument checks, the split
 // choice, workspace sizing and launches.  Nothing is enqueued unless every check passes.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -258,6 +259,44 @@ int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_by
   int S = num_splits ? num_splits : mla_dense_decode_splits(B, T, H, max_context);
   return run_decode(1, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, nullptr, B, T, H,
                     max_context, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num_pages, const int32_t* block_table,
+                        int64_t bt_stride, const int32_t* context_lens, const int32_t* indices, int32_t B, int32_t T,
+                        int32_t topk, int32_t causal, void* staged, int32_t* staged_block_table, int32_t* staged_lens,
+                        void* stream) {
+  if (!pool || !block_table || !context_lens || !indices || !staged || !staged_block_table || !staged_lens)
+    return MLA_ERR_NULL;
+  if (B < 1 || T < 1 || topk < 1 || topk > MLA_MAX_TOPK || num_pages < 1 || bt_stride < 1) return MLA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
+  if ((int64_t)B * T > ((int64_t)1 << 31) / 64) return MLA_ERR_SHAPE;
+  if (page_stride_bytes < 64LL * MLA_NVFP4_ROW_BYTES || page_stride_bytes % 16) return MLA_ERR_STRIDE_ALIGN;
+  // row addresses travel as 32-bit multiples of 16 bytes
+  if ((num_pages * page_stride_bytes) / 16 > (int64_t)0xFFFFFFFFLL) return MLA_ERR_SHAPE;
+  if (!aligned(pool, 16) || !aligned(staged, 16) || !aligned(block_table, 4) || !aligned(context_lens, 4) ||
+      !aligned(indices, 4) || !aligned(staged_block_table, 4) || !aligned(staged_lens, 4))
+    return MLA_ERR_STRIDE_ALIGN;
+  int st = check_device();
+  if (st != MLA_OK) return st;
+  mla::StageArgs a;
+  a.pool = (const uint8_t*)pool;
+  a.page_stride = page_stride_bytes;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.ctx = context_lens;
+  a.indices = indices;
+  a.B = B;
+  a.T = T;
+  a.topk = topk;
+  a.causal = causal;
+  a.pages_per_token = (int)ceil_div(topk, 64);
+  // enough workgroups to fill the chip a few times over, at most one per 128 list entries
+  a.parts = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(topk, 128), ceil_div(1024, (int64_t)B * T)));
+  a.staged = (uint8_t*)staged;
+  a.staged_block_table = staged_block_table;
+  a.staged_lens = staged_lens;
+  return mla::launch_stage(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

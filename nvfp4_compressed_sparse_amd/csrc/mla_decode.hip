@@ -95,6 +95,7 @@ struct Shared {
   uint8_t ptile[2][NH * kPStride];             // P of steps k (even/odd): [head][row], FP16
   uint32_t rowlist[DENSE ? 1 : kMaxChunk];     // sparse: row addresses of the split's valid entries
   int pages[DENSE ? kMaxChunk / kStepRows : 1];  // dense: page of each step, -1 = not in the pool
+  int fb_page;                                   // dense: page holding the row masked rows read
   float smax[2][NH][4];             // per-score-wave maxima of step k, per head
   float wsum[NH][4];                // per-score-wave softmax sums
   int flag[2];                      // step k raised the softmax reference
@@ -175,13 +176,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int e_end = lim + 1 < a.entries ? lim + 1 : a.entries;
     const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
     n_valid = e1 > e0 ? e1 - e0 : 0;
+    int pgv = -1;
     if (tid < a.chunk / kStepRows) {
       const int p = (e0 >> 6) + tid;
       const int pg = p < a.bt_stride ? btg[p] : -1;
-      sh.pages[tid] = pg >= 0 && pg < a.num_pages ? pg : -1;
+      pgv = pg >= 0 && pg < a.num_pages && tid * kStepRows < n_valid ? pg : -1;
+      sh.pages[tid] = pgv;
     }
+    // masked rows are never read from unwritten memory (bytes 0x7F/0xFF decode to NaN, and a zero
+    // weight times NaN is NaN): they are redirected to the first row of the split's first step whose
+    // page is in the pool; a split without one selects nothing
+    const uint64_t okb = __ballot(pgv >= 0);  // wave 0 holds every step (at most 32)
+    const int fbv = __shfl(pgv, okb ? (int)__builtin_ctzll(okb) : 0, 64);
+    if (tid == 0) sh.fb_page = okb ? fbv : -1;
     wait_vmem();      // the query DMA has landed
     __syncthreads();  // staged pages and queries visible
+    if (sh.fb_page < 0) n_valid = 0;
   } else {
   // ---- prologue, sparse: valid rows of this split -> LDS list of 16-byte row addresses.
   // The request's whole page-table row (it does not depend on the context length) is staged in LDS
@@ -260,9 +270,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < EPT; ++k)
     if (vmask & (1u << k)) sh.rowlist[off++] = addr[k];
-  // the list is padded to whole steps with the pool's first row, so that gathers need no bounds
-  // checks (the scores of the padding rows are masked)
-  if (tid < ((n_valid + kStepRows - 1) & -kStepRows) - n_valid) sh.rowlist[n_valid + tid] = 0u;
   // every load issued so far (indices, page table, the query DMA) has landed before the gathers start
   wait_vmem();
   __syncthreads();  // row list and staged queries complete; the page-table staging area is free again
@@ -288,18 +295,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   auto issue_step = [&](int st) {  // the gathering role only
     const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
     if constexpr (DENSE) {
-      // one page per step (a page outside the pool reads the pool's first page; its rows are masked)
+      // one page per step; the rows of a masked step, or past the context in the last step, read the
+      // split's fallback row instead (their scores are masked)
       const int pg = __builtin_amdgcn_readfirstlane(sh.pages[st]);
-      const uint8_t* base = a.pool + (pg >= 0 ? (uint64_t)pg * (uint64_t)a.page_stride : 0ull);
+      if (pg >= 0 && (st + 1) * kStepRows <= n_valid) {
+        const uint8_t* base = a.pool + (uint64_t)pg * (uint64_t)a.page_stride;
 #pragma unroll
-      for (int u = 0; u < NL; ++u)
-        if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(base + g_off[u], dst + 1024 * u);
+        for (int u = 0; u < NL; ++u)
+          if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(base + g_off[u], dst + 1024 * u);
+      } else {
+        const uint8_t* base = a.pool + (uint64_t)(pg >= 0 ? pg : 0) * (uint64_t)a.page_stride;
+        const uint8_t* fb = a.pool + (uint64_t)sh.fb_page * (uint64_t)a.page_stride;
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+          const int rin = G::kWaveRows * r4 + g_row[u];
+          const bool live = pg >= 0 && st * kStepRows + rin < n_valid;
+          const uint8_t* src = live ? base + g_off[u] : fb + (g_off[u] - (uint32_t)(rin * ROWB));
+          if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(src, dst + 1024 * u);
+        }
+      }
     } else {
       const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
-      // every row address is read first (one LDS round trip), then the loads go out
+      // every row address is read first (one LDS round trip), then the loads go out; rows past the list
+      // (last step only) read its first row (their scores are masked)
       uint32_t a16[NL];
+      if ((st + 1) * kStepRows <= n_valid) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
+        for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
+      } else {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+          const int r = st * kStepRows + G::kWaveRows * r4 + g_row[u];
+          a16[u] = sh.rowlist[r < n_valid ? r : 0];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const uint8_t* src = a.pool + ((uint64_t)a16[u] * 16u + g_off[u]);

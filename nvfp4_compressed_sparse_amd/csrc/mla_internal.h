@@ -41,6 +41,22 @@ struct DecodeArgs {
   int* counters;              // [B*T*head groups] split arrival counters, zero between calls
 };
 
+struct StageArgs {
+  const uint8_t* pool;        // NVFP4 page pool
+  int64_t page_stride;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* ctx;         // [B]
+  const int32_t* indices;     // [B,T,topk]
+  int B, T, topk, causal;
+  int pages_per_token;        // P = ceil(topk / 64)
+  int parts;                  // workgroups per query token
+  uint8_t* staged;            // FP8 pool of B*T*P pages of 64 x 576 bytes
+  int32_t* staged_block_table;  // [B*T, P]
+  int32_t* staged_lens;       // [B*T]
+};
+
 // Which decode kernel serves a shape: the wide-head kernel for NVFP4 rows with 64 or 128 heads (every
 // row dequantized once for all heads), the 16/32-head-group kernel otherwise.
 inline bool uses_wide_kernel(int fmt, int H) { return fmt == 0 && (H == 64 || H == 128); }
@@ -49,5 +65,7 @@ hipError_t launch_quant(int fmt, const QuantArgs& a, hipStream_t stream);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream);
 // 64 or 128 heads: one workgroup per (query token, split) covers every head (mla_decode_wide.hip).
 hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream);
+// The staged path's unpack of each query token's selected NVFP4 rows into FP8 rows (mla_stage.hip).
+hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 
 }  // namespace mla

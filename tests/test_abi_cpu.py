@@ -143,3 +143,29 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         M.mla_kv_quant_nvfp4(torch.zeros(1, 512, dtype=torch.bfloat16), torch.zeros(1, 64, dtype=torch.bfloat16),
                              torch.zeros(1, dtype=torch.int64), torch.zeros(22528, dtype=torch.uint8), 22528, 1)
+
+
+def _stage(**kw):
+    a = dict(pool=FAKE, ps=64 * 352, npg=10, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, B=2, T=1, k=256, causal=0,
+             staged=FAKE, sbt=FAKE, slen=FAKE, stream=None)
+    a.update(kw)
+    return M.lib().mla_stage_nvfp4_fp8(a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"], a["idx"], a["B"],
+                                       a["T"], a["k"], a["causal"], a["staged"], a["sbt"], a["slen"], a["stream"])
+
+
+def test_stage_argument_errors():
+    for name in ("pool", "bt", "ctx", "idx", "staged", "sbt", "slen"):
+        assert _stage(**{name: None}) == 1, name
+    assert _stage(B=0) == 2
+    assert _stage(T=0) == 2
+    assert _stage(k=0) == 2
+    assert _stage(k=2049) == 2
+    assert _stage(causal=2) == 2
+    assert _stage(npg=0) == 2
+    assert _stage(ps=64 * 352 - 16) == 3
+    assert _stage(ps=64 * 352 + 8) == 3
+    assert _stage(staged=FAKE + 8) == 3
+    assert _stage(slen=FAKE + 2) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert _stage() == 5  # valid arguments reach the device check

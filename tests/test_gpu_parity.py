@@ -330,6 +330,117 @@ def test_dense_fp8_pages_outside_the_pool():
         say(compare_outputs(out, ro, lse, rl, f"dense invalid pages S={S}"))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_unwritten_pool_bytes_do_not_leak(fmt):
+    """Pool bytes no row was written to hold 0xFF (NaN as E4M3): the rows a decode gathers but masks
+    (past the list in the last step, past the context on a last page, pages outside the pool) must not
+    reach the output."""
+    H = 32 if fmt == "nvfp4" else 128
+    cfg = small(B=3, T=1, H=H, topk=300 if fmt == "nvfp4" else 0, L=1000, fmt=fmt, seed=45)
+    case = Case(cfg, ctx=[1000, 333, 70])
+    if fmt == "fp8":
+        case.lay.block_table[0, 4] = -1
+    say(f"unwritten pool bytes {fmt}")
+    d = case.to_device()
+    d["pool"].fill_(0xFF)
+    gpu_pool(case, d)
+    for S in (1, 3):
+        out, lse = gpu_decode(case, d, num_splits=S)
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(out, ro, lse, rl, f"0xFF pool {fmt} S={S}"))
+
+
+# --------------------------------------------------------------------------- staged path (NVFP4 -> FP8 copy)
+def _gpu_stage(pool_d, page_stride, num_pages, bt_d, ctx_d, idx_d, causal=False):
+    staged, sbt, slen = M.mla_stage_nvfp4_fp8(pool_d, page_stride, num_pages, bt_d, ctx_d, idx_d, causal=causal)
+    torch.cuda.synchronize()
+    nq, P = sbt.shape
+    return staged.cpu().numpy().reshape(nq, P * 64, 576), sbt.cpu().numpy(), slen.cpu().numpy()
+
+
+def _check_staged(staged, sbt, slen, ref_staged, ref_counts):
+    nq, P = sbt.shape
+    assert np.array_equal(slen, ref_counts)
+    assert np.array_equal(sbt, np.arange(nq)[:, None] * P + np.arange(P)[None, :])
+    for i in range(nq):
+        n = int(ref_counts[i])
+        if not np.array_equal(staged[i, :n], ref_staged[i, :n]):
+            bad = np.argwhere(staged[i, :n] != ref_staged[i, :n])[:5]
+            raise AssertionError(f"token {i}: staged bytes differ at {bad.tolist()}: "
+                                 f"{[(int(staged[i][tuple(x)]), int(ref_staged[i][tuple(x)])) for x in bad]}")
+
+
+def test_stage_every_scale_and_nibble_bit_exact():
+    """Every (scale byte, nibble) pair the format can hold, NaN scale bytes aside, unpacked to FP8 bit
+    for bit as the oracle does it (including products above 448, -0 and E4M3 subnormals)."""
+    rows = []
+    for r in range(8):
+        row = np.zeros(352, np.uint8)
+        for j in range(32):
+            sc = 32 * r + j
+            row[256 + j] = 0 if sc in (0x7F, 0xFF) else sc
+            nib = np.arange(16, dtype=np.uint8)
+            row[8 * j:8 * j + 8] = nib[0::2] | (nib[1::2] << 4)
+        row[288:352] = (np.arange(64) * 7 + r).astype(np.uint8)
+        rows.append(row)
+    pool = np.zeros(2 * 64 * 352, np.uint8)
+    pool[64 * 352:64 * 352 + 8 * 352] = np.concatenate(rows)
+    bt = np.array([[1]], np.int32)
+    ctx = np.array([8], np.int32)
+    idx = np.array([[[7, 0, 3, 5, 1, 6, 2, 4]]], np.int32)
+    ref, cnt = oracle.stage_nvfp4_fp8(pool, 64 * 352, 2, bt, ctx, idx)
+    say("stage every scale x nibble")
+    got = _gpu_stage(torch.from_numpy(pool).cuda(), 64 * 352, 2, torch.from_numpy(bt).cuda(),
+                     torch.from_numpy(ctx).cuda(), torch.from_numpy(idx).cuda())
+    _check_staged(*got, ref, cnt)
+
+
+@pytest.mark.parametrize("T,causal", [(1, False), (2, True)])
+def test_stage_selection_bit_exact(T, causal):
+    """Selection (padding, entries past the context, pages outside the pool), order and bytes of the
+    staged copy, several tokens, topk not a multiple of 64."""
+    cfg = small(B=3, T=T, H=16, topk=300, L=2000, causal=causal, seed=43)
+    case = Case(cfg, ctx=[2000, 650, 90])
+    idx = case.idx.copy()
+    idx[0, 0, :37] = -1
+    idx[1, -1, 10:20] = 10 ** 7
+    case.idx = idx
+    case.lay.block_table[0, 5] = -3
+    say(f"stage selection T={T} causal={causal}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    ref, cnt = oracle.stage_nvfp4_fp8(case.oracle_pool(), cfg.page_stride, case.lay.num_pages, case.lay.block_table,
+                                      case.lay.ctx, idx, causal=causal)
+    got = _gpu_stage(d["pool"], cfg.page_stride, case.lay.num_pages, d["bt"], d["ctx"], d["idx"], causal=causal)
+    _check_staged(*got, ref, cnt)
+
+
+@pytest.mark.parametrize("H", [16, 32, 128])
+def test_staged_decode_matches_oracle(H):
+    """The staged path end to end: the GPU copy read by the GPU FP8 decoder against the oracle's FP8
+    attention over the oracle's copy."""
+    cfg = small(B=4, T=1, H=H, topk=512, L=5000, seed=44)
+    case = Case(cfg, ctx=[5000, 3000, 900, 400])
+    say(f"staged decode H={H}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    staged, sbt, slen = M.mla_stage_nvfp4_fp8(d["pool"], cfg.page_stride, case.lay.num_pages, d["bt"], d["ctx"],
+                                              d["idx"])
+    nq, P = sbt.shape
+    q1 = d["q"].view(nq, 1, H, 576)
+    lse = torch.empty((nq, 1, H), dtype=torch.float32, device="cuda")
+    out, _ = M.mla_dense_decode_fp8(q1, staged, 64 * 576, nq * P, sbt, slen, P * 64, cfg.sm_scale, lse=lse)
+    torch.cuda.synchronize()
+    ref_st, cnt = oracle.stage_nvfp4_fp8(case.oracle_pool(), cfg.page_stride, case.lay.num_pages,
+                                         case.lay.block_table, case.lay.ctx, case.idx)
+    bt = (np.arange(nq)[:, None] * P + np.arange(P)[None, :]).astype(np.int32)
+    ro, rl, _ = oracle.dense_decode_fp8(case.q.reshape(nq, 1, H, 576), ref_st.reshape(-1), 64 * 576, nq * P, bt, cnt,
+                                        cfg.sm_scale)
+    say(compare_outputs(bf16_to_np(out).reshape(nq, H, 512), ro,
+                        lse.cpu().numpy().astype(np.float64).reshape(nq, H), rl, f"staged decode H={H}"))
+
+
 # --------------------------------------------------------------------------- full-size configs, sampled
 def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
     """Oracle results for sampled query tokens of a full-size device case: the selected source rows are

@@ -66,6 +66,9 @@ CONFIGS = {
                          seed=20260004),
     "mixed": DecodeConfig("mixed", B=256, T=1, H=128, topk=2048, fmt="nvfp4", ctx_range=(8192, 146000),
                           quant_chunk=4096, alloc_tokens=146000, seed=20260005),
+    # the pages' native-vs-staged comparison shape: 15 query tokens per launch, one TP4 rank of a 64-head
+    # model (16 heads), ~140K-token agent contexts, top-2048
+    "pages15": DecodeConfig("pages15", B=15, T=1, H=16, topk=2048, fmt="nvfp4", ctx=140000, seed=20260006),
 }
 
 
