@@ -39,11 +39,16 @@ int head_groups(int32_t H) { return H == 16 ? 1 : H / 32; }
 constexpr int kTargetWorkgroups = 256;  // one resident workgroup per compute unit
 constexpr int kMaxSplits = 64;
 constexpr int kMaxChunk = 2048;  // list entries one workgroup can hold
-constexpr int kTileRows = 64;
+constexpr int kMinSplitEntries = 256;  // four 64-row steps
 
+// Split count of the 16/32-head-group kernel: as many splits as fit one workgroup per compute unit
+// (never more workgroups than units: a second round of workgroups costs a whole split's latency), and at
+// least 256 list entries per split (a split of one or two steps is mostly fixed latency, and every
+// extra split adds to what the merging workgroup reads).  Measured at 15/20/35 query tokens with 16
+// heads, top-2048: 8, 8 and 7 splits against 18, 13 and 8 before, 20-32% faster.
 int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
-  int64_t s = ceil_div(kTargetWorkgroups, units);
-  int64_t cap = ceil_div(entries, kTileRows);
+  int64_t s = kTargetWorkgroups / units;
+  int64_t cap = ceil_div(entries, kMinSplitEntries);
   if (s > cap) s = cap;
   if (s < min_splits) s = min_splits;
   if (s > kMaxSplits) s = kMaxSplits;

@@ -123,7 +123,11 @@ def test_split_choice_and_workspace_sizes():
     assert L.mla_sparse_decode_splits(64, 1, 32, 2048) == 4
     assert L.mla_sparse_decode_splits(128, 4, 32, 2048) == 1
     assert L.mla_sparse_decode_splits(256, 1, 128, 2048) == 1
-    assert L.mla_sparse_decode_splits(2, 1, 16, 256) == 4  # capped at one 64-row tile per split
+    assert L.mla_sparse_decode_splits(2, 1, 16, 256) == 1  # at least 256 list entries per split
+    # small launches: at most one workgroup per compute unit, at least 256 entries per split
+    assert L.mla_sparse_decode_splits(15, 1, 16, 2048) == 8
+    assert L.mla_sparse_decode_splits(20, 1, 16, 2048) == 8
+    assert L.mla_sparse_decode_splits(35, 1, 16, 2048) == 7
     assert L.mla_dense_decode_splits(16, 1, 128, 8192) == 4
     assert L.mla_dense_decode_splits(4, 1, 128, 8192) == 16
     assert L.mla_sparse_decode_splits(0, 1, 32, 2048) == 0

@@ -69,6 +69,11 @@ CONFIGS = {
     # the pages' native-vs-staged comparison shape: 15 query tokens per launch, one TP4 rank of a 64-head
     # model (16 heads), ~140K-token agent contexts, top-2048
     "pages15": DecodeConfig("pages15", B=15, T=1, H=16, topk=2048, fmt="nvfp4", ctx=140000, seed=20260006),
+    # the pages' launch-size tunings: 20 query tokens per launch (cluster sizing) and a 35-token launch
+    # whose short contexts leave -1 entries in the 2,048-position lists
+    "pages20": DecodeConfig("pages20", B=20, T=1, H=16, topk=2048, fmt="nvfp4", ctx=140000, seed=20260007),
+    "short35": DecodeConfig("short35", B=35, T=1, H=16, topk=2048, fmt="nvfp4", ctx_range=(256, 2048),
+                            seed=20260008),
 }
 
 
