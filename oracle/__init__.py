@@ -167,7 +167,9 @@ def kv_quant(fmt: str, k_nope: np.ndarray, k_rope: np.ndarray, slot_mapping: np.
     n = sl.shape[0]
     assert kn.shape == (n, LATENT) and kr.shape == (n, ROPE)
     row_bytes = NVFP4_ROW_BYTES if fmt == "nvfp4" else FP8_ROW_BYTES
-    assert page_stride >= PAGE * row_bytes and pool.size >= num_pages * page_stride
+    # the last page's rows end PAGE rows into it (a pool may be one layer of a block-major cache, whose
+    # page stride spans every layer's rows)
+    assert page_stride >= PAGE * row_bytes and pool.size >= (num_pages - 1) * page_stride + PAGE * row_bytes
     f = _load().mlo_kv_quant_nvfp4 if fmt == "nvfp4" else _load().mlo_kv_quant_fp8
     return f(_ptr(kn), LATENT, _ptr(kr), ROPE, _ptr(sl), n, _ptr(pool), page_stride, num_pages)
 
