@@ -106,8 +106,10 @@ def _quant(fn_name, k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_p
         raise ValueError("k_rope must be [n, 64] with unit inner stride")
     if not slot_mapping.is_contiguous() or not pool.is_contiguous():
         raise ValueError("slot_mapping and pool must be contiguous")
-    if pool.numel() < page_stride_bytes * num_pages:
-        raise ValueError("pool smaller than num_pages * page_stride_bytes")
+    row_bytes = NVFP4_ROW_BYTES if fn_name == "mla_kv_quant_nvfp4" else FP8_ROW_BYTES
+    # the last page's 64 rows must lie inside the pool (which may be one layer of a block-major cache)
+    if num_pages < 1 or pool.numel() < page_stride_bytes * (num_pages - 1) + PAGE_TOKENS * row_bytes:
+        raise ValueError("pool too small for num_pages pages of page_stride_bytes")
     st = getattr(lib(), fn_name)(k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
                                  slot_mapping.data_ptr(), n, pool.data_ptr(), int(page_stride_bytes), int(num_pages),
                                  _stream(stream))

@@ -351,6 +351,51 @@ def test_unwritten_pool_bytes_do_not_leak(fmt):
         say(compare_outputs(out, ro, lse, rl, f"0xFF pool {fmt} S={S}"))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_block_major_multi_layer_pool(fmt):
+    """Block-major pages (the analysis page's KV layout section: all layers of a block adjacent): page p
+    holds layer 0's 64 rows, then layer 1's, ...; layer l is the pool shifted by l x 64 rows with a page
+    stride of n_layers x 64 rows.  Each layer's writes and decodes touch only its own rows."""
+    n_layers = 3
+    H = 32 if fmt == "nvfp4" else 128
+    cfg = small(B=2, T=1, H=H, topk=384 if fmt == "nvfp4" else 0, L=1500, fmt=fmt, seed=46)
+    rb = cfg.row_bytes
+    stride = n_layers * 64 * rb
+    cases = [Case(cfg, seed_offset=l) for l in range(n_layers)]
+    lay = cases[0].lay
+    for c in cases[1:]:  # one page table for every layer, as in a block-major cache
+        c.lay = lay
+        c.slots = np.concatenate([W.slots_for_request(lay, b, np.arange(int(lay.ctx[b]))) for b in range(cfg.B)])
+    say(f"block-major {n_layers} layers {fmt}")
+    pool = torch.full((lay.num_pages * stride,), 0xFF, dtype=torch.uint8, device="cuda")
+    ref_pool = np.zeros(lay.num_pages * stride, np.uint8)
+    quant = M.mla_kv_quant_nvfp4 if fmt == "nvfp4" else M.mla_kv_quant_fp8
+    for l, c in enumerate(cases):
+        d = c.to_device()
+        quant(d["lat"], d["rope"], d["slots"], pool[l * 64 * rb:], stride, lay.num_pages)
+        oracle.kv_quant(fmt, c.lat, c.rope, c.slots, ref_pool[l * 64 * rb:], stride, lay.num_pages)
+    torch.cuda.synchronize()
+    host = pool.cpu().numpy()
+    written = ref_pool != 0
+    assert np.array_equal(host[written], ref_pool[written])
+    for l, c in enumerate(cases):
+        d = c.to_device()
+        lse = torch.empty((cfg.B, 1, H), dtype=torch.float32, device="cuda")
+        if fmt == "nvfp4":
+            out, _ = M.mla_sparse_decode(d["q"], pool[l * 64 * rb:], stride, lay.num_pages, d["bt"], d["ctx"], d["idx"],
+                                         cfg.sm_scale, lse=lse)
+            ro, rl, _ = oracle.sparse_decode(c.q, ref_pool[l * 64 * rb:], stride, lay.num_pages, lay.block_table,
+                                             lay.ctx, c.idx, cfg.sm_scale)
+        else:
+            out, _ = M.mla_dense_decode_fp8(d["q"], pool[l * 64 * rb:], stride, lay.num_pages, d["bt"], d["ctx"],
+                                            int(lay.ctx.max()), cfg.sm_scale, lse=lse)
+            ro, rl, _ = oracle.dense_decode_fp8(c.q, ref_pool[l * 64 * rb:], stride, lay.num_pages, lay.block_table,
+                                                lay.ctx, cfg.sm_scale)
+        torch.cuda.synchronize()
+        say(compare_outputs(bf16_to_np(out).reshape(cfg.B, H, 512), ro,
+                            lse.cpu().numpy().astype(np.float64).reshape(cfg.B, H), rl, f"layer {l}"))
+
+
 # --------------------------------------------------------------------------- staged path (NVFP4 -> FP8 copy)
 def _gpu_stage(pool_d, page_stride, num_pages, bt_d, ctx_d, idx_d, causal=False):
     staged, sbt, slen = M.mla_stage_nvfp4_fp8(pool_d, page_stride, num_pages, bt_d, ctx_d, idx_d, causal=causal)
