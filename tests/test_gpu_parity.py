@@ -535,7 +535,7 @@ def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
     return np.stack(outs), np.stack(lses), pools_ok
 
 
-@pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b16"])
+@pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b16", "pages15", "short35"])
 def test_full_size_config_sampled(name):
     cfg = W.CONFIGS[name]
     say(f"full-size {name}: generating inputs")
@@ -580,3 +580,54 @@ def test_full_size_config_sampled(name):
             assert np.array_equal(grows[r], oracle.quant_row_nvfp4(cl[r], cr[r]))
     del inp, pool
     torch.cuda.empty_cache()
+
+
+def test_full_size_staged_path_sampled():
+    """The staged path at the primary config's full size, as bench.py --path staged times it: for sampled
+    query tokens, the FP8 copy is bit-exact against the oracle's unpack of the token's selected rows (the
+    oracle quantizes the source rows itself), and the FP8 decode over the GPU copy matches the oracle's
+    FP8 attention over its own copy."""
+    cfg = W.CONFIGS["sparse"]
+    say("full-size staged: generating inputs")
+    inp = W.device_inputs(cfg, "cuda", n_sets=1)
+    lay = inp["layout"]
+    pool = torch.zeros(lay.num_pages * cfg.page_stride, dtype=torch.uint8, device="cuda")
+    M.mla_kv_quant_nvfp4(inp["lat"], inp["rope"], inp["slots"], pool, cfg.page_stride, lay.num_pages)
+    idx = inp["idx_sets"][0]
+    q = inp["q_sets"][0]
+    nq = cfg.B * cfg.T
+    say("full-size staged: stage + FP8 decode")
+    staged, sbt, slen = M.mla_stage_nvfp4_fp8(pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx)
+    P = sbt.shape[1]
+    lse = torch.empty((nq, 1, cfg.H), dtype=torch.float32, device="cuda")
+    out, _ = M.mla_dense_decode_fp8(q.view(nq, 1, cfg.H, 576), staged, 64 * 576, nq * P, sbt, slen, P * 64,
+                                    cfg.sm_scale, lse=lse)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    q_h = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    lens = slen.cpu().numpy()
+    g_out = bf16_to_np(out).reshape(nq, cfg.H, 512)
+    g_lse = lse.cpu().numpy().astype(np.float64).reshape(nq, cfg.H)
+    qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed + 1).choice(nq, 4, replace=False))))
+    say(f"full-size staged: oracle on query tokens {qtoks}")
+    for qt in qtoks:
+        b, t = divmod(int(qt), cfg.T)
+        lim = W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal)
+        ids = idx_h[b, t]
+        pos = ids[(ids >= 0) & (ids <= lim)]  # list order, as staged
+        n = pos.size
+        assert lens[qt] == n
+        rows = torch.from_numpy(inp["row_off"][b] + pos).cuda()
+        lat = inp["lat"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        rope = inp["rope"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        npg = (n + 63) // 64
+        mini = np.zeros(npg * 64 * 352, np.uint8)
+        oracle.kv_quant("nvfp4", lat, rope, np.arange(n, dtype=np.int64), mini, 64 * 352, npg)
+        ref, cnt = oracle.stage_nvfp4_fp8(mini, 64 * 352, npg, np.arange(npg, dtype=np.int32)[None, :],
+                                          np.array([n], np.int32), np.arange(n, dtype=np.int32).reshape(1, 1, n))
+        got = staged[qt * P * 64 * 576:(qt * P * 64 + n) * 576].cpu().numpy().reshape(n, 576)
+        assert cnt[0] == n and np.array_equal(got, ref[0, :n]), f"staged rows of query token {qt}"
+        ro, rl, _ = oracle.dense_decode_fp8(q_h[b:b + 1, t:t + 1], ref[0].reshape(-1), 64 * 576, ref.shape[1] // 64,
+                                            np.arange(ref.shape[1] // 64, dtype=np.int32)[None, :],
+                                            np.array([n], np.int32), cfg.sm_scale)
+        say(compare_outputs(g_out[qt:qt + 1], ro, g_lse[qt:qt + 1], rl, f"staged token {qt}"))
