@@ -6,7 +6,9 @@ nothing from the GPU path.
 
 Each function documents the passage it follows; mla_oracle.c's header lists the pages and the
 readings taken where they are silent.  Arrays cross the boundary as numpy arrays on the host:
-bf16 values travel as their uint16 bit patterns.
+bf16 values travel as their uint16 bit patterns.  The index selection (topk_positions) is plain numpy
+here; the pages fix only its size (2,048) and the -1 padding, and its tie rule and list order are
+readings stated in its docstring.  The indexer's logits, which the pages do not define, are an input.
 """
 from __future__ import annotations
 
@@ -249,3 +251,29 @@ def stage_nvfp4_fp8(pool, page_stride, num_pages, block_table, ctx, indices, cau
     _load().mlo_stage_nvfp4_fp8(_ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T,
                                 k, int(bool(causal)), R, _ptr(staged), _ptr(counts))
     return staged, counts
+
+
+# --------------------------------------------------------------------------- index selection (top-k)
+
+def topk_positions(logits, lengths, k):
+    """The sparse indexer's last step (launch post, native NVFP4 sparse MLA decode section: each query
+    token attends to at most 2,048 positions the indexer selects, -1 marking unused list entries; the
+    analysis page, section "Decode: TP4, and the copies it keeps": index_topk 2048): for each row, the
+    positions i < lengths[r] of the k largest logits[r, i], compared as numbers (-0 equals +0).
+    Readings where the pages are silent: ties at the k-th value go to the lower positions, and the list
+    is in ascending position order (the decode reads it as a set); a row with at most k positions lists
+    them all, then -1.  logits float32 [n, ld] (no NaN), lengths int [n] (0 <= lengths <= ld).
+    Returns int32 [n, k]."""
+    x = np.asarray(logits, dtype=np.float32)
+    n = x.shape[0]
+    out = np.full((n, k), -1, np.int32)
+    for r in range(n):
+        m = int(lengths[r])
+        if m <= 0:
+            continue
+        v = x[r, :m].astype(np.float64)
+        pos = np.arange(m)
+        order = np.lexsort((pos, -v))  # by value descending, then by position ascending
+        chosen = np.sort(order[:min(k, m)])
+        out[r, :chosen.size] = chosen
+    return out

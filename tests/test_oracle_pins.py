@@ -591,3 +591,49 @@ def test_staged_decode_close_to_native_decode():
     rel = np.linalg.norm(o_st - o_na) / np.linalg.norm(o_na)
     assert 0 < rel < 0.05, rel
     assert np.abs(l_st - l_na).max() < 0.5
+
+
+# --------------------------------------------------------------------------- index selection (top-k)
+def test_topk_positions_brute_force_small():
+    """Tiny rows with many ties, -0.0 next to +0.0 and infinities: the right count of positions, in
+    ascending order, -1 after them, and no unchosen position beats a chosen one under the order
+    (value, then lower position) -- with Python's float comparison, in which -0.0 equals 0.0."""
+    rng = np.random.default_rng(50)
+    for trial in range(200):
+        m = int(rng.integers(0, 12))
+        k = int(rng.integers(1, 8))
+        # few distinct values, so that ties are common; some infinities
+        vals = rng.choice(np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 2.0, np.inf], np.float32), size=max(m, 1))
+        logits = np.zeros((1, 12), np.float32)
+        logits[0, :m] = vals[:m]
+        got = oracle.topk_positions(logits, [m], k)[0]
+        chosen = [int(p) for p in got if p >= 0]
+        assert len(chosen) == min(k, m)
+        assert chosen == sorted(chosen)
+        assert np.all(got[len(chosen):] == -1)
+        rest = [p for p in range(m) if p not in chosen]
+        for c in chosen:
+            for o in rest:  # an unchosen position is never strictly better
+                assert (vals[o], -o) < (vals[c], -c), (trial, c, o)
+
+
+def test_topk_positions_properties():
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((3, 5000)).astype(np.float32)
+    x[1, ::7] = 1.5  # a large tie block straddling the threshold
+    lens = [5000, 4000, 100]
+    got = oracle.topk_positions(x, lens, 2048)
+    for r, m in enumerate(lens):
+        sel = got[r][got[r] >= 0]
+        assert sel.size == min(2048, m)
+        assert np.all(np.diff(sel) > 0) and sel.max() < m
+        thr = np.sort(x[r, :m])[::-1][min(2048, m) - 1]
+        assert np.all(x[r, sel] >= thr)
+        assert np.sum(x[r, :m] > thr) <= sel.size
+        outside = np.setdiff1d(np.arange(m), sel)
+        if outside.size:
+            assert np.all(x[r, outside] <= thr)
+            ties_in = sel[x[r, sel] == thr]
+            ties_out = outside[x[r, outside] == thr]
+            if ties_in.size and ties_out.size:
+                assert ties_in.max() < ties_out.min()  # ties go to lower positions
