@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--op", default="decode", choices=["decode", "index-topk"],
+                    help="decode: the decode step (default); index-topk: the indexer's top-k selection over fp32 "
+                         "logits of the workload's query tokens and contexts")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
@@ -120,6 +123,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in DESIGN.md "
                                    "but not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.op == "index-topk":
+        bench_index_topk(args)
+        return
 
     import torch
     import nvfp4_compressed_sparse_amd as M
@@ -292,6 +298,101 @@ def main():
     }
     if cpu is not None:
         res["cpu_baseline"] = run_cpu_baseline(cfg, cpu)
+    print(json.dumps(res), flush=True)
+
+
+def bench_index_topk(args):
+    """The index top-k over one step's logits: B*T query tokens, each over its context, top-`topk`."""
+    import torch
+    import nvfp4_compressed_sparse_amd as M
+
+    cfg = W.CONFIGS[args.workload]
+    if not cfg.topk:
+        raise SystemExit("--op index-topk applies to the sparse workloads")
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    rng = np.random.default_rng(cfg.seed)
+    ctx = W.context_lengths(cfg, rng)
+    n = cfg.B * cfg.T
+    # each query token ranks the positions it may attend to (its causal limit, or the whole context)
+    lengths = np.array([W.position_limit(int(ctx[b]), cfg.T, t, cfg.causal) + 1 for b in range(cfg.B)
+                        for t in range(cfg.T)], np.int32)
+    ld = int(-(-int(lengths.max()) // 4) * 4)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    sets = [W.torch_logits(gen, n, ld, dev) for _ in range(N_SETS)]
+    lens_d = torch.from_numpy(lengths).to(dev)
+    out = torch.empty((n, cfg.topk), dtype=torch.int32, device=dev)
+    ws = torch.zeros(M.mla_index_topk_workspace_bytes(n, ld), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] index top-k: {n} rows, ld={ld}, k={cfg.topk}, {N_SETS} logit sets of "
+        f"{n * ld * 4 / 1e6:.1f} MB")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.mla_index_topk(sets[i % N_SETS], lens_d, cfg.topk, out=out, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    chosen = int((out >= 0).sum().item())
+    if chosen != int(np.minimum(lengths, cfg.topk).sum()):
+        raise SystemExit(f"index top-k chose {chosen} positions, expected {int(np.minimum(lengths, cfg.topk).sum())}")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    call_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    call_avg = float(np.mean(call_us))
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step; call avg {call_avg:.2f} us, "
+        f"p10 {np.percentile(call_us, 10):.2f}, p90 {np.percentile(call_us, 90):.2f}")
+    # algorithmic bytes: every logit of every row read once, the lists written
+    bytes_per = int(lengths.astype(np.int64).sum() * 4 + n * cfg.topk * 4)
+    ach = bytes_per / (call_avg * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "mla_index_topk call: topk_hist_kernel, topk_collect_kernel, topk_finish_kernel, timed together with HIP "
+                      "events on their stream",
+            "algorithmic_bytes_per_launch": bytes_per, "launch_us": round(call_avg, 3)}
+    res = {
+        "metric": "index top-k query-tokens/s (fp32 logits over each context, top-%d); %% of roofline" % cfg.topk,
+        "value": round(n / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": n, "context": cfg.ctx or list(cfg.ctx_range), "ld": ld,
+                   "topk": cfg.topk, "logits": "N(0,1) fp32", "step": "index top-k"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        x = sets[0].cpu().numpy()
+        rows = min(n, args.cpu_sample or n)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.topk_positions(x[:rows], lengths[:rows], cfg.topk)
+            times.append(time.perf_counter() - t0)
+        tmed = float(np.median(times))
+        res["cpu_baseline"] = {"value": round(rows / tmed, 3), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {n} rows of one step, median of 3 runs of {tmed:.2f} s "
+                                         "(numpy, one thread)"}
     print(json.dumps(res), flush=True)
 
 

@@ -108,8 +108,10 @@ int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context
  * log-sum-exps of the splits.  The last workgroup of a query token to finish merges its splits in the
  * same launch (the pages merge a cluster's partial results without a second launch either).
  * A workspace must be ZERO-FILLED before its first use; every call returns the counters to zero, so
- * a workspace can then be reused by any later call on the same stream (any shape).  Two calls that can
- * run concurrently must not share a workspace. */
+ * a workspace can then be reused without refilling by later calls on the same stream with the same
+ * B, T, H and split count.  A call of another shape may place its counters where an earlier call
+ * wrote partial results: zero-fill the workspace again before such a call.  Two calls that can run
+ * concurrently must not share a workspace. */
 size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits);
 
@@ -180,6 +182,37 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
                         int64_t bt_stride, const int32_t* context_lens, const int32_t* indices, int32_t B, int32_t T,
                         int32_t topk, int32_t causal, void* staged, int32_t* staged_block_table, int32_t* staged_lens,
                         void* stream);
+
+/*
+ * Index top-k: the sparse indexer's selection step that produces the decoders' index lists (launch post:
+ * a query token attends to at most 2,048 cached positions picked by the indexer, unused entries -1; the
+ * analysis page, section "Decode: TP4, and the copies it keeps": index_topk 2048).  The pages do not define the
+ * indexer's logits; this call takes them as an input.  For each row r < n with m = lengths[r]:
+ *   out[r][:] = the positions i < m of the k largest logits[r*ld + i], ties at the k-th largest value
+ *               going to the lower positions, in ascending order; when m <= k, out[r] = 0, 1, ..., m-1
+ *               followed by k - m entries of -1.
+ * Values are compared as numbers (-0 equals +0; -inf and +inf are ordinary values); NaN logits are outside
+ * the contract (the output is then still k distinct positions below m, or the short-row list).
+ *   logits     (device) fp32, row r at logits + r*ld, 16-byte aligned; only positions below lengths[r] are
+ *              read
+ *   ld         row stride in elements: a multiple of 4, at least every lengths[r]; lengths[r] outside
+ *              [0, ld] are clamped to it
+ *   lengths    (device) int32 [n]
+ *   n          rows (query tokens), >= 0; n = 0 does nothing
+ *   k          1..2048
+ *   out        (device) int32 [n, k], 4-byte aligned
+ *   workspace  (device) >= mla_index_topk_workspace_bytes(n, ld) bytes, 256-byte aligned, zero-filled
+ *              before its first use.  Every call returns its per-row histograms and counters to zero, so the
+ *              workspace can be reused without refilling by later calls on the same stream with the same n
+ *              and ld (zero-fill it again before a call with another n or ld).  Concurrent calls must not
+ *              share a workspace.
+ * Errors: MLA_ERR_SHAPE (n < 0, k outside 1..2048, ld above 2^31-1, too many rows x chunks of 8192
+ * positions), MLA_ERR_STRIDE_ALIGN (ld not a positive multiple of 4, misaligned pointers), MLA_ERR_NULL,
+ * MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+size_t mla_index_topk_workspace_bytes(int64_t n, int64_t ld);
+int mla_index_topk(const float* logits, int64_t ld, const int32_t* lengths, int64_t n, int32_t k, int32_t* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

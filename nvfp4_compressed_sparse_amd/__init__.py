@@ -23,7 +23,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8",
+    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_index_topk_workspace_bytes",
+    "mla_index_topk",
 ]
 
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
         "mla_stage_nvfp4_fp8": (ctypes.c_int, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, P, P, P, P]),
+        "mla_index_topk_workspace_bytes": (sz, [i64, i64]),
+        "mla_index_topk": (ctypes.c_int, [P, i64, P, i64, i32, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -248,3 +251,40 @@ def mla_stage_nvfp4_fp8(pool, page_stride_bytes, num_pages, block_table, context
                                    staged_lens.data_ptr(), _stream(stream))
     _check("mla_stage_nvfp4_fp8", st)
     return staged, staged_block_table, staged_lens
+
+
+# --------------------------------------------------------------------------- index top-k
+
+def mla_index_topk_workspace_bytes(n, ld):
+    return lib().mla_index_topk_workspace_bytes(int(n), int(ld))
+
+
+def mla_index_topk(logits, lengths, k, out=None, workspace=None, stream=None):
+    """Per row of fp32 logits [n, ld] (contiguous, ld a multiple of 4), the positions below
+    lengths[r] of the k largest values, lower positions first among ties, in ascending order and padded
+    with -1 (see include/mla_nvfp4.h).  Returns int32 [n, k].  A workspace passed in must be a uint8
+    device tensor zero-filled before its first use; one is allocated (zero-filled) when none is."""
+    import torch
+    _dev(logits, torch.float32, "logits")
+    _dev(lengths, torch.int32, "lengths")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        # contiguous, so that the device-side clamp of lengths to ld keeps every read inside the tensor
+        raise ValueError("logits must be a contiguous [n, ld] tensor")
+    n, ld = logits.shape
+    if lengths.numel() != n or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous [n] tensor")
+    if out is None:
+        out = torch.empty((n, int(k)), dtype=torch.int32, device=logits.device)
+    _dev(out, torch.int32, "out")
+    if tuple(out.shape) != (n, int(k)) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n, k] int32 tensor")
+    if n == 0:
+        return out
+    ws = lib().mla_index_topk_workspace_bytes(n, ld)
+    if workspace is None:
+        workspace = torch.zeros(ws, dtype=torch.uint8, device=logits.device)  # counters start at zero
+    _dev(workspace, torch.uint8, "workspace")
+    st = lib().mla_index_topk(logits.data_ptr(), ld, lengths.data_ptr(), n, int(k), out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check("mla_index_topk", st)
+    return out

@@ -2,6 +2,7 @@
 // choice, workspace sizing and launches.  Nothing is enqueued unless every check passes.
 #include <algorithm>
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <atomic>
@@ -92,6 +93,23 @@ WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
 }
 
 size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) { return workspace_layout(B, T, H, S).total; }
+
+// Index top-k workspace: [histograms n*2^11 int32][counters n*4 int32] (the part kept at zero between
+// calls), then [segments n*chunks int2][candidates n*kTopkCap uint2], each region 256-byte aligned.
+struct TopkLayout {
+  size_t ctrl_off, seg_off, cand_off, total;
+};
+
+TopkLayout topk_layout(int64_t n, int64_t ld) {
+  TopkLayout l{0, 0, 0, 0};
+  if (n < 1 || ld < 1) return l;
+  const size_t chunks = (size_t)ceil_div(ld, mla::kTopkChunk);
+  l.ctrl_off = round256((size_t)n * ((size_t)1 << mla::kTopkBits1) * sizeof(int32_t));
+  l.seg_off = l.ctrl_off + round256((size_t)n * mla::kTopkCtrlInts * sizeof(int32_t));
+  l.cand_off = l.seg_off + round256((size_t)n * chunks * 2 * sizeof(int32_t));
+  l.total = l.cand_off + round256((size_t)n * mla::kTopkCap * 2 * sizeof(uint32_t));
+  return l;
+}
 
 int check_quant(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
                 const int64_t* slot_mapping, int64_t n, void* pool, int64_t page_stride, int64_t num_pages,
@@ -302,6 +320,39 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
   a.staged_block_table = staged_block_table;
   a.staged_lens = staged_lens;
   return mla::launch_stage(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_index_topk_workspace_bytes(int64_t n, int64_t ld) { return topk_layout(n, ld).total; }
+
+int mla_index_topk(const float* logits, int64_t ld, const int32_t* lengths, int64_t n, int32_t k, int32_t* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || k < 1 || k > MLA_MAX_TOPK) return MLA_ERR_SHAPE;
+  if (ld < 4 || ld % 4) return MLA_ERR_STRIDE_ALIGN;
+  if (ld > INT32_MAX) return MLA_ERR_SHAPE;  // positions are int32
+  const int64_t chunks = ceil_div(ld, mla::kTopkChunk);
+  if (n * chunks > INT32_MAX) return MLA_ERR_SHAPE;  // one workgroup per chunk of every row
+  if (n == 0) return MLA_OK;
+  if (!logits || !lengths || !out || !workspace) return MLA_ERR_NULL;
+  if (!aligned(logits, 16) || !aligned(lengths, 4) || !aligned(out, 4) || !aligned(workspace, 256))
+    return MLA_ERR_STRIDE_ALIGN;
+  const TopkLayout l = topk_layout(n, ld);
+  if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE;
+  int st = check_device();
+  if (st != MLA_OK) return st;
+  mla::TopkArgs a;
+  a.logits = logits;
+  a.n = n;
+  a.ld = ld;
+  a.lengths = lengths;
+  a.k = k;
+  a.chunks = (int)chunks;
+  a.out = out;
+  char* ws = (char*)workspace;
+  a.hist = (int*)ws;
+  a.ctrl = (int*)(ws + l.ctrl_off);
+  a.seg = (int2*)(ws + l.seg_off);
+  a.cand = (uint2*)(ws + l.cand_off);
+  return mla::launch_topk(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -57,6 +57,28 @@ struct StageArgs {
   int32_t* staged_lens;       // [B*T]
 };
 
+// Index top-k (mla_topk.hip).  Workspace per row: a histogram of the top kTopkBits1 key bits and
+// kTopkCtrlInts counters (both zero between calls), one segment (start, count) per kTopkChunk positions,
+// and kTopkCap candidate (key, position) pairs.
+constexpr int kTopkChunk = 8192;
+constexpr int kTopkBits1 = 11;
+constexpr int kTopkCap = 8192;
+constexpr int kTopkCtrlInts = 4;
+
+struct TopkArgs {
+  const float* logits;        // [n, ld]
+  int64_t n;
+  int64_t ld;
+  const int32_t* lengths;     // [n]
+  int k;
+  int chunks;                 // ceil(ld / kTopkChunk)
+  int32_t* out;               // [n, k]
+  int* hist;                  // [n, 1 << kTopkBits1]
+  int* ctrl;                  // [n, kTopkCtrlInts]: candidate cursor, level-1 bin, count above it, candidates
+  int2* seg;                  // [n, chunks]
+  uint2* cand;                // [n, kTopkCap]
+};
+
 // Which decode kernel serves a shape: the wide-head kernel for NVFP4 rows with 64 or 128 heads (every
 // row dequantized once for all heads), the 16/32-head-group kernel otherwise.
 inline bool uses_wide_kernel(int fmt, int H) { return fmt == 0 && (H == 64 || H == 128); }
@@ -67,5 +89,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream);
 // The staged path's unpack of each query token's selected NVFP4 rows into FP8 rows (mla_stage.hip).
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
+// The three launches of the index top-k (mla_topk.hip).
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -173,3 +173,42 @@ def test_stage_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert _stage() == 5  # valid arguments reach the device check
+
+
+def _topk(**kw):
+    a = dict(x=FAKE, ld=4096, lens=FAKE, n=4, k=2048, out=FAKE, ws=FAKE, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = M.lib().mla_index_topk_workspace_bytes(a["n"], a["ld"])
+    return M.lib().mla_index_topk(a["x"], a["ld"], a["lens"], a["n"], a["k"], a["out"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+def test_index_topk_argument_errors():
+    for name in ("x", "lens", "out", "ws"):
+        assert _topk(**{name: None}) == 1, name
+    assert _topk(n=-1) == 2
+    assert _topk(k=0) == 2
+    assert _topk(k=2049) == 2
+    assert _topk(ld=(1 << 31) + 4) == 2
+    assert _topk(ld=4094) == 3
+    assert _topk(ld=0) == 3
+    assert _topk(x=FAKE + 4) == 3
+    assert _topk(out=FAKE + 2) == 3
+    assert _topk(ws=FAKE + 16) == 3
+    assert _topk(wsb=M.lib().mla_index_topk_workspace_bytes(4, 4096) - 1) == 4
+    assert _topk(n=0, x=None, lens=None, out=None, ws=None) == 0  # nothing to do
+    import torch
+    if not torch.cuda.is_available():
+        assert _topk() == 5  # valid arguments reach the device check
+
+
+def test_index_topk_workspace_size():
+    # per row: 2^11 histogram bins and 4 counters (int32), a segment per 8192 positions (2 x int32) and 8192
+    # candidates (2 x int32), each region rounded up to 256 bytes
+    r256 = lambda x: (x + 255) // 256 * 256
+    for n, ld in [(1, 4), (64, 140000), (3, 8192), (3, 8196)]:
+        chunks = -(-ld // 8192)
+        want = r256(n * 2048 * 4) + r256(n * 16) + r256(n * chunks * 8) + r256(n * 8192 * 8)
+        assert M.lib().mla_index_topk_workspace_bytes(n, ld) == want, (n, ld)
+    assert M.lib().mla_index_topk_workspace_bytes(0, 4096) == 0

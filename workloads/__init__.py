@@ -14,6 +14,11 @@ these inputs stand in for it with the pages' shapes):
     leaves fewer than topk positions the rest is -1;
   * page table: the ceil(L/64) logical pages of every request map to a random permutation of the
     physical pages; physical page 0 is a pad page no request uses; unused table entries are -1.
+  * index logits (the input of the index top-k; the pages do not define the indexer's logits): one
+    fp32 row per query token over its context, ld = context rounded up to a multiple of 4, values by
+    kind: "normal" N(0,1); "coarse" N(0,1) rounded to multiples of 1/16 (ties at the threshold);
+    "ties" integers 0..3 (bins far larger than the candidate buffer); "equal" all 0.5; "special" a mix
+    of -0.0, +0.0, +-inf, subnormals, +-FLT_MAX and N(0,1).
 CPU generators use numpy PCG64; device generators use a seeded torch generator on the GPU.
 """
 from __future__ import annotations
@@ -185,6 +190,12 @@ def torch_bf16_normal(gen, shape, device, scale_rows=False, outliers=False):
     return x.to(torch.bfloat16)
 
 
+def torch_logits(gen, n: int, ld: int, device):
+    """Seeded N(0,1) fp32 [n, ld] index logits on the device (the "normal" kind)."""
+    import torch
+    return torch.randn((n, ld), generator=gen, device=device, dtype=torch.float32)
+
+
 def torch_indices(gen, ctx: np.ndarray, T: int, topk: int, causal: bool, device):
     """[B,T,topk] int32 on the device: distinct uniform positions in [0, limit], random order, -1 pad."""
     import torch
@@ -250,3 +261,27 @@ def device_inputs(cfg: DecodeConfig, device="cuda", n_sets: int = 1, row_chunk: 
         out["chunk_rope"] = torch_bf16_normal(gen, (cfg.quant_chunk, ROPE), device)
         out["chunk_slots"] = torch.from_numpy(gen_chunk_slots(lay, rng, cfg.quant_chunk)).to(device)
     return out
+
+
+# --------------------------------------------------------------------------- index logits
+LOGIT_KINDS = ("normal", "coarse", "ties", "equal", "special")
+
+
+def gen_logits(rng: np.random.Generator, n: int, ld: int, kind: str = "normal") -> np.ndarray:
+    """fp32 [n, ld] logits of one kind (see the module recipe)."""
+    if kind == "normal":
+        return rng.standard_normal((n, ld), dtype=np.float32)
+    if kind == "coarse":
+        return np.round(rng.standard_normal((n, ld), dtype=np.float32) * 16.0) / np.float32(16.0)
+    if kind == "ties":
+        return rng.integers(0, 4, (n, ld)).astype(np.float32)
+    if kind == "equal":
+        return np.full((n, ld), 0.5, np.float32)
+    if kind == "special":
+        specials = np.array([-0.0, 0.0, np.inf, -np.inf, 1e-45, -1e-45, 1e-40, -1e-40, 3.4028235e38, -3.4028235e38],
+                            np.float32)
+        x = rng.standard_normal((n, ld), dtype=np.float32)
+        pick = rng.random((n, ld)) < 0.3
+        x[pick] = specials[rng.integers(0, specials.size, int(pick.sum()))]
+        return x
+    raise ValueError(kind)
