@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--op", default="decode", choices=["decode", "index-topk"],
                     help="decode: the decode step (default); index-topk: the indexer's top-k selection over fp32 "
                          "logits of the workload's query tokens and contexts")
+    ap.add_argument("--logits", default="normal", choices=["normal", "ramp"],
+                    help="index-topk: N(0,1) logits, or N(0,1) plus a rising trend over positions")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
@@ -320,7 +322,7 @@ def bench_index_topk(args):
     ld = int(-(-int(lengths.max()) // 4) * 4)
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
-    sets = [W.torch_logits(gen, n, ld, dev) for _ in range(N_SETS)]
+    sets = [W.torch_logits(gen, n, ld, dev, args.logits) for _ in range(N_SETS)]
     lens_d = torch.from_numpy(lengths).to(dev)
     out = torch.empty((n, cfg.topk), dtype=torch.int32, device=dev)
     ws = torch.zeros(M.mla_index_topk_workspace_bytes(n, ld), dtype=torch.uint8, device=dev)
@@ -359,8 +361,8 @@ def bench_index_topk(args):
     ach = bytes_per / (call_avg * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "mla_index_topk call: topk_hist_kernel, topk_collect_kernel, topk_finish_kernel, timed together with HIP "
-                      "events on their stream",
+            "kernel": "mla_index_topk call: topk_hist_kernel, topk_collect_kernel, topk_finish_kernel, timed with HIP events "
+                      "on their stream",
             "algorithmic_bytes_per_launch": bytes_per, "launch_us": round(call_avg, 3)}
     res = {
         "metric": "index top-k query-tokens/s (fp32 logits over each context, top-%d); %% of roofline" % cfg.topk,
@@ -376,7 +378,8 @@ def bench_index_topk(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "rows": n, "context": cfg.ctx or list(cfg.ctx_range), "ld": ld,
-                   "topk": cfg.topk, "logits": "N(0,1) fp32", "step": "index top-k"},
+                   "topk": cfg.topk, "logits": "N(0,1) fp32" if args.logits == "normal" else
+                   "N(0,1) + 6 * position / ld, fp32", "step": "index top-k"},
         "roofline": roof,
         "cpu_baseline": None,
     }

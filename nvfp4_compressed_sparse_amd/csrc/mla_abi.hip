@@ -94,7 +94,7 @@ WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
 
 size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) { return workspace_layout(B, T, H, S).total; }
 
-// Index top-k workspace: [histograms n*2^11 int32][counters n*4 int32] (the part kept at zero between
+// Index top-k workspace: [histograms n*2^12 int32][counters n*8 int32] (the part kept at zero between
 // calls), then [segments n*chunks int2][candidates n*kTopkCap uint2], each region 256-byte aligned.
 struct TopkLayout {
   size_t ctrl_off, seg_off, cand_off, total;

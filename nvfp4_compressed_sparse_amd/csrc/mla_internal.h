@@ -58,12 +58,12 @@ struct StageArgs {
 };
 
 // Index top-k (mla_topk.hip).  Workspace per row: a histogram of the top kTopkBits1 key bits and
-// kTopkCtrlInts counters (both zero between calls), one segment (start, count) per kTopkChunk positions,
+// kTopkCtrlInts counters (both zero between calls), one segment (slot, count) per kTopkChunk positions,
 // and kTopkCap candidate (key, position) pairs.
 constexpr int kTopkChunk = 8192;
-constexpr int kTopkBits1 = 11;
+constexpr int kTopkBits1 = 12;
 constexpr int kTopkCap = 8192;
-constexpr int kTopkCtrlInts = 4;
+constexpr int kTopkCtrlInts = 8;
 
 struct TopkArgs {
   const float* logits;        // [n, ld]
@@ -74,8 +74,9 @@ struct TopkArgs {
   int chunks;                 // ceil(ld / kTopkChunk)
   int32_t* out;               // [n, k]
   int* hist;                  // [n, 1 << kTopkBits1]
-  int* ctrl;                  // [n, kTopkCtrlInts]: candidate cursor, level-1 bin, count above it, candidates
-  int2* seg;                  // [n, chunks]
+  int* ctrl;                  // [n, kTopkCtrlInts]: candidate cursor, level-1 bin, count above it,
+                              // candidate count, histogram arrival counter
+  int2* seg;                  // [n, chunks]: candidate slot, count
   uint2* cand;                // [n, kTopkCap]
 };
 

@@ -204,11 +204,11 @@ def test_index_topk_argument_errors():
 
 
 def test_index_topk_workspace_size():
-    # per row: 2^11 histogram bins and 4 counters (int32), a segment per 8192 positions (2 x int32) and 8192
-    # candidates (2 x int32), each region rounded up to 256 bytes
+    # per row: 2^12 histogram bins and 8 counters (int32), a segment per 8192 positions (2 x int32) and
+    # 8192 candidates (2 x int32), each region rounded up to 256 bytes
     r256 = lambda x: (x + 255) // 256 * 256
     for n, ld in [(1, 4), (64, 140000), (3, 8192), (3, 8196)]:
         chunks = -(-ld // 8192)
-        want = r256(n * 2048 * 4) + r256(n * 16) + r256(n * chunks * 8) + r256(n * 8192 * 8)
+        want = r256(n * 4096 * 4) + r256(n * 32) + r256(n * chunks * 8) + r256(n * 8192 * 8)
         assert M.lib().mla_index_topk_workspace_bytes(n, ld) == want, (n, ld)
     assert M.lib().mla_index_topk_workspace_bytes(0, 4096) == 0

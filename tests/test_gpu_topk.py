@@ -68,7 +68,7 @@ def test_index_topk_workspace_reuse():
         x = W.gen_logits(rng, n, ldim, kind)
         got = run(x, LENS, 2048, workspace=ws)
         assert np.array_equal(got, oracle.topk_positions(x, LENS, 2048)), (i, kind)
-    assert int(ws[: n * 2048 * 4 + n * 16].count_nonzero()) == 0
+    assert int(ws[: n * 4096 * 4 + n * 32].count_nonzero()) == 0
 
 
 def test_index_topk_full_size():

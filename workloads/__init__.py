@@ -18,7 +18,8 @@ these inputs stand in for it with the pages' shapes):
     fp32 row per query token over its context, ld = context rounded up to a multiple of 4, values by
     kind: "normal" N(0,1); "coarse" N(0,1) rounded to multiples of 1/16 (ties at the threshold);
     "ties" integers 0..3 (bins far larger than the candidate buffer); "equal" all 0.5; "special" a mix
-    of -0.0, +0.0, +-inf, subnormals, +-FLT_MAX and N(0,1).
+    of -0.0, +0.0, +-inf, subnormals, +-FLT_MAX and N(0,1); "ramp" N(0,1) + 6 * position / ld (the
+    largest values crowd into the last positions, as a recency trend would put them).
 CPU generators use numpy PCG64; device generators use a seeded torch generator on the GPU.
 """
 from __future__ import annotations
@@ -190,10 +191,15 @@ def torch_bf16_normal(gen, shape, device, scale_rows=False, outliers=False):
     return x.to(torch.bfloat16)
 
 
-def torch_logits(gen, n: int, ld: int, device):
-    """Seeded N(0,1) fp32 [n, ld] index logits on the device (the "normal" kind)."""
+def torch_logits(gen, n: int, ld: int, device, kind: str = "normal"):
+    """Seeded fp32 [n, ld] index logits on the device: the "normal" or the "ramp" kind."""
     import torch
-    return torch.randn((n, ld), generator=gen, device=device, dtype=torch.float32)
+    x = torch.randn((n, ld), generator=gen, device=device, dtype=torch.float32)
+    if kind == "ramp":
+        x += 6.0 * torch.arange(ld, device=device, dtype=torch.float32) / ld
+    elif kind != "normal":
+        raise ValueError(kind)
+    return x
 
 
 def torch_indices(gen, ctx: np.ndarray, T: int, topk: int, causal: bool, device):
@@ -264,7 +270,7 @@ def device_inputs(cfg: DecodeConfig, device="cuda", n_sets: int = 1, row_chunk: 
 
 
 # --------------------------------------------------------------------------- index logits
-LOGIT_KINDS = ("normal", "coarse", "ties", "equal", "special")
+LOGIT_KINDS = ("normal", "coarse", "ties", "equal", "special", "ramp")
 
 
 def gen_logits(rng: np.random.Generator, n: int, ld: int, kind: str = "normal") -> np.ndarray:
@@ -284,4 +290,7 @@ def gen_logits(rng: np.random.Generator, n: int, ld: int, kind: str = "normal") 
         pick = rng.random((n, ld)) < 0.3
         x[pick] = specials[rng.integers(0, specials.size, int(pick.sum()))]
         return x
+    if kind == "ramp":
+        x = rng.standard_normal((n, ld), dtype=np.float32)
+        return x + (np.float32(6.0) * np.arange(ld, dtype=np.float32) / np.float32(ld))[None, :]
     raise ValueError(kind)
