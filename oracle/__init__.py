@@ -8,7 +8,8 @@ Each function documents the passage it follows; mla_oracle.c's header lists the 
 readings taken where they are silent.  Arrays cross the boundary as numpy arrays on the host:
 bf16 values travel as their uint16 bit patterns.  The index selection (topk_positions) is plain numpy
 here; the pages fix only its size (2,048) and the -1 padding, and its tie rule and list order are
-readings stated in its docstring.  The indexer's logits, which the pages do not define, are an input.
+readings stated in its docstring.  index_logits is PARITY UNPINNED: the pages do not define the
+indexer's logits, and the function computes the DeepSeek-style form named in its docstring.
 """
 from __future__ import annotations
 
@@ -57,6 +58,9 @@ def _load():
         "mlo_e4m3_encode_bulk": (None, [P, i64, P]),
         "mlo_scale_code_bulk": (None, [P, i64, P]),
         "mlo_quant_row_nvfp4": (None, [P, P, P]),
+        "mlo_index_key_quant_row": (None, [P, P, P]),
+        "mlo_index_key_quant": (i64, [P, i64, P, i64, P, i64, i64]),
+        "mlo_index_logits": (i32, [P, P, i32, P, i64, i64, P, i64, P, i32, i32, i32, P, i64, i32]),
         "mlo_quant_row_fp8": (None, [P, P, P]),
         "mlo_dequant_row_nvfp4": (None, [P, P]),
         "mlo_dequant_row_fp8": (None, [P, P]),
@@ -251,6 +255,53 @@ def stage_nvfp4_fp8(pool, page_stride, num_pages, block_table, ctx, indices, cau
     _load().mlo_stage_nvfp4_fp8(_ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T,
                                 k, int(bool(causal)), R, _ptr(staged), _ptr(counts))
     return staged, counts
+
+
+# --------------------------------------------------------------------------- sparse indexer keys and logits
+INDEX_DIM = 128
+INDEX_PAGE_BYTES = PAGE * INDEX_DIM + PAGE * 4  # 64 rows of 128 codes, then 64 fp32 scales
+
+
+def index_key_quant(keys, slot_mapping, pool, page_stride, num_pages):
+    """Indexer keys (analysis page, "Four bits per latent value: where 352 comes from": 128 FP8 values
+    plus a scale per token; the quantization is the TokenSpeed write-up's per-token FP8 rule, a reading):
+    keys bf16 bits [n, 128] into the paged indexer pool (uint8, modified in place).  Returns the number
+    of keys written."""
+    k = np.ascontiguousarray(keys, dtype=np.uint16)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k.ndim == 2 and k.shape[1] == INDEX_DIM and sm.shape == (k.shape[0],)
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    assert page_stride >= INDEX_PAGE_BYTES and pool.size >= page_stride * (num_pages - 1) + INDEX_PAGE_BYTES
+    return _load().mlo_index_key_quant(_ptr(k), INDEX_DIM, _ptr(sm), k.shape[0], _ptr(pool), page_stride, num_pages)
+
+
+def index_key_quant_row(x):
+    """One key: bf16 bits [128] -> (codes uint8 [128], fp32 scale)."""
+    xv = np.ascontiguousarray(x, dtype=np.uint16)
+    codes = np.zeros(INDEX_DIM, np.uint8)
+    sc = np.zeros(1, np.float32)
+    _load().mlo_index_key_quant_row(_ptr(xv), _ptr(codes), _ptr(sc))
+    return codes, float(sc[0])
+
+
+def index_logits(q, w, pool, page_stride, num_pages, block_table, ctx, causal=False, ld=None, nthreads=0):
+    """Indexer logits, PARITY UNPINNED: the pages do not define them; this is the DeepSeek-style form
+    the analysis page points to.  logits[b*T+t, p] = s_p * sum_j w[b,t,j] * max(0, <q[b,t,j], k_p>)
+    for p up to the query token's limit (k_p: the key's E4M3 values, s_p its scale), -inf on page
+    entries outside the pool, NaN past the limit.  q bf16 bits [B,T,HI,128], w float32 [B,T,HI].
+    Returns float64 [B*T, ld]."""
+    qv = np.ascontiguousarray(q, dtype=np.uint16)
+    wv = np.ascontiguousarray(w, dtype=np.float32)
+    B, T, HI, D = qv.shape
+    assert D == INDEX_DIM and wv.shape == (B, T, HI)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cx = np.ascontiguousarray(ctx, dtype=np.int32)
+    if ld is None:
+        ld = int(cx.max()) if cx.size else 0
+    out = np.full((B * T, ld), np.nan, np.float64)
+    _load().mlo_index_logits(_ptr(qv), _ptr(wv), HI, _ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1],
+                             _ptr(cx), B, T, int(bool(causal)), _ptr(out), ld, nthreads)
+    return out
 
 
 # --------------------------------------------------------------------------- index selection (top-k)

@@ -30,6 +30,16 @@
  *    ignored (as if absent); an empty selection gives out = 0 and lse = -inf;
  *  - duplicates count once per occurrence (plain multiset softmax).
  *
+ * Sparse indexer (analysis page, section "Four bits per latent value: where 352 comes from": the
+ * indexer keeps 128 FP8 values plus a scale per token on the layers that have one, stored the way
+ * DeepSeek's indexer is; the launch post and the analysis page: each query token keeps at most 2,048
+ * positions).  The pages give the key size, not the quantization or the logits; readings:
+ *  - key quantization as in the TokenSpeed write-up's per-token FP8 path (its MLA KV layout section):
+ *    in fp32, s = max(amax, 1e-26) / 448, each value E4M3(x / s) nearest with ties to even, saturating;
+ *    page layout: 64 rows of 128 code bytes, then 64 fp32 scales;
+ *  - logits, PARITY UNPINNED (no page defines them; the DeepSeek-style form the analysis page points
+ *    to): logit(p) = s_p * sum_j w_j * max(0, <q_j, e4m3(code_p)>) over the index heads j.
+ *
  * Floating point: everything in double.  Encoding decisions are exact: distances between a bf16
  * input and a candidate grid value are computed exactly in double (the bit span of both operands
  * fits in 53 bits inside the guarded range; outside it the nearest value is fixed by saturation or
@@ -377,6 +387,86 @@ void mlo_stage_nvfp4_fp8(const uint8_t* pool, int64_t page_stride, int64_t num_p
     }
     counts[id] = n;
   }
+}
+
+/* ------------------------------------------------------------------ sparse indexer */
+
+#define IDX_DIM 128
+#define IDX_PAGE_CODES (PAGE * IDX_DIM) /* scales follow the 64 code rows of a page */
+
+/* One indexer key: 128 bf16 values -> 128 E4M3 codes and an fp32 scale (fp32 arithmetic, as the
+ * per-token FP8 path computes it).  The codes are the nearest E4M3 values to the fp32 quotients,
+ * with the input's sign. */
+void mlo_index_key_quant_row(const uint16_t* x, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < IDX_DIM; ++i) {
+    float v = fabsf((float)mlo_bf16_value(x[i]));
+    if (v > amax) amax = v;
+  }
+  float s = (amax > 1e-26f ? amax : 1e-26f) / 448.0f;
+  for (int i = 0; i < IDX_DIM; ++i) {
+    float y = (float)mlo_bf16_value(x[i]) / s;
+    uint32_t sign = (x[i] >> 15) & 1;
+    codes[i] = (uint8_t)((sign << 7) | nearest_e4m3_code(fabs((double)y), 1.0));
+  }
+  *scale = s;
+}
+
+/* Write n indexer keys into a paged pool (page p at pool + p*page_stride: 64 rows of 128 code bytes,
+ * then 64 fp32 scales).  Negative slots and slots on pages outside [0, num_pages) are skipped.
+ * key_stride in elements. */
+int64_t mlo_index_key_quant(const uint16_t* keys, int64_t key_stride, const int64_t* slot_mapping, int64_t n,
+                            uint8_t* pool, int64_t page_stride, int64_t num_pages) {
+  int64_t written = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t slot = slot_mapping[r];
+    if (slot < 0 || slot / PAGE >= num_pages) continue;
+    uint8_t* page = pool + (slot / PAGE) * page_stride;
+    float sc;
+    mlo_index_key_quant_row(keys + r * key_stride, page + (slot % PAGE) * IDX_DIM, &sc);
+    memcpy(page + IDX_PAGE_CODES + (slot % PAGE) * 4, &sc, 4);
+    ++written;
+  }
+  return written;
+}
+
+/* Indexer logits of query token id = b*T + t (parity unpinned: the form is a reading, see the file
+ * header) over positions p <= limit: logits[id*ld + p] = s_p * sum_j w[id*HI + j] * max(0, <q_j, k_p>)
+ * with k_p the E4M3 values of the key's codes, in double.  q bf16 [B,T,HI,128], w fp32 [B,T,HI].
+ * Positions on a page entry outside [0, num_pages) get -inf; positions past the limit are left as
+ * they are. */
+int mlo_index_logits(const uint16_t* q, const float* w, int HI, const uint8_t* pool, int64_t page_stride,
+                     int64_t num_pages, const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, int B,
+                     int T, int causal, double* logits, int64_t ld, int nthreads) {
+  int used = set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t id = 0; id < (int64_t)B * T; ++id) {
+    int b = (int)(id / T), t = (int)(id % T);
+    int64_t lim = position_limit(ctx[b], T, t, causal);
+    double* qd = (double*)malloc(sizeof(double) * HI * IDX_DIM);
+    for (int64_t i = 0; i < (int64_t)HI * IDX_DIM; ++i) qd[i] = mlo_bf16_value(q[id * HI * IDX_DIM + i]);
+    for (int64_t p = 0; p <= lim && p < ld; ++p) {
+      int64_t page = block_table[(int64_t)b * bt_stride + p / PAGE];
+      if (page < 0 || page >= num_pages) {
+        logits[id * ld + p] = -INFINITY;
+        continue;
+      }
+      const uint8_t* codes = pool + page * page_stride + (p % PAGE) * IDX_DIM;
+      float sc;
+      memcpy(&sc, pool + page * page_stride + IDX_PAGE_CODES + (p % PAGE) * 4, 4);
+      double k[IDX_DIM];
+      for (int d = 0; d < IDX_DIM; ++d) k[d] = mlo_e4m3_value(codes[d]);
+      double acc = 0.0;
+      for (int j = 0; j < HI; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < IDX_DIM; ++d) dot += qd[j * IDX_DIM + d] * k[d];
+        if (dot > 0.0) acc += (double)w[id * HI + j] * dot;
+      }
+      logits[id * ld + p] = (double)sc * acc;
+    }
+    free(qd);
+  }
+  return used;
 }
 
 /* Merge S partial results of one query token computed over disjoint parts of its selection:

@@ -637,3 +637,121 @@ def test_topk_positions_properties():
             ties_out = outside[x[r, outside] == thr]
             if ties_in.size and ties_out.size:
                 assert ties_in.max() < ties_out.min()  # ties go to lower positions
+
+
+# --------------------------------------------------------------------------- indexer keys and logits
+def _bits(x):
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    v = np.asarray(x, np.float32).view(np.uint32)
+    assert np.all((v & 0xFFFF) == 0)
+    return (v >> 16).astype(np.uint16)
+
+
+def test_index_key_scale_and_codes():
+    # amax 448 -> scale exactly 1: the values themselves are encoded; 1.0625 and 1.1875 sit halfway
+    # between E4M3 neighbours and go to the even code (1.0 = 0x38, 1.25 = 0x3A)
+    x = np.zeros(128, np.float32)
+    x[:6] = [448.0, 1.0625, 1.1875, -3.0, -0.0, 0.0078125]
+    codes, s = oracle.index_key_quant_row(_bits(x))
+    assert s == 1.0
+    # 448 = 1.75 * 2^8 (e 15, m 6); -3 = -1.5 * 2^1 (e 8, m 4); 2^-7 is the subnormal m = 4
+    assert list(codes[:6]) == [0x7E, 0x38, 0x3A, 0xC4, 0x80, 0x04]
+    assert all(c == 0 for c in codes[6:])
+    # amax 3: scale is the fp32 quotient 3/448, the largest value maps to 448
+    x = np.zeros(128, np.float32)
+    x[7] = -3.0
+    codes, s = oracle.index_key_quant_row(_bits(x))
+    assert s == float(np.float32(3.0) / np.float32(448.0))
+    assert codes[7] == 0xFE and all(c == 0 for i, c in enumerate(codes) if i != 7)
+    # an all-zero key: the clamped scale, every code zero (the sign of -0 kept)
+    x = np.zeros(128, np.float32)
+    x[1] = -0.0
+    codes, s = oracle.index_key_quant_row(_bits(x))
+    assert s == float(np.float32(1e-26) / np.float32(448.0))
+    assert codes[0] == 0 and codes[1] == 0x80
+
+
+def test_index_key_round_trip():
+    """Decoded values stay within half an E4M3 step of the quotient x / s (relative 1/16 for normal
+    values, 2^-10 absolute below 2^-6), and the largest magnitude decodes to 448 * s."""
+    rng = np.random.default_rng(60)
+    for _ in range(50):
+        x = (rng.standard_normal(128) * np.exp(rng.uniform(-8, 8))).astype(np.float32)
+        xb = _bits((x.view(np.uint32) & 0xFFFF0000).view(np.float32))
+        codes, s = oracle.index_key_quant_row(xb)
+        xv = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        dec = np.array([oracle._load().mlo_e4m3_value(int(c)) for c in codes])
+        y = xv / s
+        err = np.abs(dec - y)
+        assert np.all(err <= np.maximum(np.abs(y) / 16, 2.0 ** -10) * (1 + 1e-9))
+        assert np.abs(dec).max() == 448.0
+
+
+def _index_pool(keys_codes, scales, page_stride=oracle.INDEX_PAGE_BYTES):
+    """A pool whose page i holds rows 64i.. of the given codes / scales (identity page table)."""
+    n = keys_codes.shape[0]
+    pages = (n + 63) // 64
+    pool = np.zeros(pages * page_stride, np.uint8)
+    for r in range(n):
+        base = (r // 64) * page_stride
+        pool[base + (r % 64) * 128: base + (r % 64) * 128 + 128] = keys_codes[r]
+        pool[base + 8192 + (r % 64) * 4: base + 8192 + (r % 64) * 4 + 4] = np.frombuffer(np.float32(scales[r]).tobytes(), np.uint8)
+    return pool, pages
+
+
+def test_index_logits_closed_forms():
+    # three keys: key 0 has code 0x38 (1.0) at dim 5, key 1 code 0xB8 (-1.0) at dim 5, key 2 code 0x40
+    # (2.0) at dim 9; scales 0.5, 1, 4
+    codes = np.zeros((3, 128), np.uint8)
+    codes[0, 5], codes[1, 5], codes[2, 9] = 0x38, 0xB8, 0x40
+    pool, pages = _index_pool(codes, [0.5, 1.0, 4.0])
+    bt = np.arange(pages, dtype=np.int32)[None, :]
+    q = np.zeros((1, 1, 2, 128), np.float32)
+    q[0, 0, 0, 5] = 3.0   # head 0 looks at dim 5
+    q[0, 0, 1, 9] = -1.0  # head 1 looks at dim 9 with a negative sign
+    w = np.array([[[2.0, 5.0]]], np.float32)
+    lg = oracle.index_logits(_bits(q), w, pool, oracle.INDEX_PAGE_BYTES, pages, bt, [3])
+    # key 0: head 0 dot 3*1 = 3 -> 2*3 = 6, head 1 dot 0; times 0.5 -> 3
+    # key 1: head 0 dot -3 -> ReLU 0; head 1 dot 0 -> 0
+    # key 2: head 0 dot 0; head 1 dot -2 -> ReLU 0 -> 0
+    assert list(lg[0]) == [3.0, 0.0, 0.0]
+    q[0, 0, 1, 9] = 1.5   # now head 1 sees key 2: 1.5*2 = 3, weight 5 -> 15, scale 4 -> 60
+    lg = oracle.index_logits(_bits(q), w, pool, oracle.INDEX_PAGE_BYTES, pages, bt, [3])
+    assert list(lg[0]) == [3.0, 0.0, 60.0]
+    # a negative weight can make a logit negative; the ReLU acts on the dot product, not on the sum
+    w2 = np.array([[[2.0, -5.0]]], np.float32)
+    lg = oracle.index_logits(_bits(q), w2, pool, oracle.INDEX_PAGE_BYTES, pages, bt, [3])
+    assert list(lg[0]) == [3.0, 0.0, -60.0]
+
+
+def test_index_logits_structure():
+    """Linearity in the head weights, proportionality to the key scale, the causal limit and pages
+    outside the pool, on random keys."""
+    rng = np.random.default_rng(61)
+    L, HI, T = 150, 4, 2
+    keys = _bits((rng.standard_normal((L, 128)).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32))
+    pool = np.zeros(3 * oracle.INDEX_PAGE_BYTES, np.uint8)
+    oracle.index_key_quant(keys, np.arange(L), pool, oracle.INDEX_PAGE_BYTES, 3)
+    bt = np.array([[0, 1, 2]], np.int32)
+    q = _bits((rng.standard_normal((1, T, HI, 128)).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32))
+    # multiples of 1/64 below 8 in magnitude: w1 + w2 is exact in fp32
+    w1 = (np.round(rng.standard_normal((1, T, HI)) * 64) / 64).astype(np.float32)
+    w2 = (np.round(rng.standard_normal((1, T, HI)) * 64) / 64).astype(np.float32)
+    a = oracle.index_logits(q, w1, pool, oracle.INDEX_PAGE_BYTES, 3, bt, [L], causal=True)
+    b = oracle.index_logits(q, w2, pool, oracle.INDEX_PAGE_BYTES, 3, bt, [L], causal=True)
+    c = oracle.index_logits(q, w1 + w2, pool, oracle.INDEX_PAGE_BYTES, 3, bt, [L], causal=True)
+    ok = ~np.isnan(c)
+    assert np.allclose(c[ok], (a + b)[ok], rtol=1e-12, atol=1e-12)
+    # causal: token 0 sees positions 0..L-2, token 1 sees 0..L-1
+    assert np.isnan(a[0, L - 1]) and not np.isnan(a[1, L - 1]) and not np.isnan(a[0, L - 2])
+    # doubling every scale doubles every logit
+    pool2 = pool.copy()
+    for pg in range(3):
+        sc = pool2[pg * oracle.INDEX_PAGE_BYTES + 8192: pg * oracle.INDEX_PAGE_BYTES + 8448].view(np.float32)
+        sc *= 2
+    d = oracle.index_logits(q, w1, pool2, oracle.INDEX_PAGE_BYTES, 3, bt, [L], causal=True)
+    assert np.array_equal(d[ok], 2 * a[ok])
+    # a page entry outside the pool gives -inf for its 64 positions
+    bt_bad = np.array([[0, 7, 2]], np.int32)
+    e = oracle.index_logits(q, w1, pool, oracle.INDEX_PAGE_BYTES, 3, bt_bad, [L], causal=True)
+    assert np.all(e[:, 64:128] == -np.inf) and np.array_equal(e[:, :64], a[:, :64])
