@@ -111,9 +111,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
-    ap.add_argument("--op", default="decode", choices=["decode", "index-topk"],
+    ap.add_argument("--op", default="decode", choices=["decode", "index-topk", "index-logits"],
                     help="decode: the decode step (default); index-topk: the indexer's top-k selection over fp32 "
-                         "logits of the workload's query tokens and contexts")
+                         "logits of the workload's query tokens and contexts; index-logits: the indexer's logits "
+                         "over FP8 keys (a DeepSeek-style reading)")
+    ap.add_argument("--index-heads", type=int, default=64, help="index-logits: index heads (16, 32 or 64)")
     ap.add_argument("--logits", default="normal", choices=["normal", "ramp"],
                     help="index-topk: N(0,1) logits, or N(0,1) plus a rising trend over positions")
     args = ap.parse_args()
@@ -127,6 +129,9 @@ def main():
         sys.exit(2)
     if args.op == "index-topk":
         bench_index_topk(args)
+        return
+    if args.op == "index-logits":
+        bench_index_logits(args)
         return
 
     import torch
@@ -396,6 +401,125 @@ def bench_index_topk(args):
         res["cpu_baseline"] = {"value": round(rows / tmed, 3), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
                                "sample": f"{rows} of {n} rows of one step, median of 3 runs of {tmed:.2f} s "
                                          "(numpy, one thread)"}
+    print(json.dumps(res), flush=True)
+
+
+def bench_index_logits(args):
+    """The indexer's logits for one step: B*T query tokens, each over the FP8 keys of its request's
+    context (128 codes + an fp32 scale per position), HI index heads."""
+    import torch
+    import nvfp4_compressed_sparse_amd as M
+
+    cfg = W.CONFIGS[args.workload]
+    if not cfg.topk:
+        raise SystemExit("--op index-logits applies to the sparse workloads")
+    HI = args.index_heads
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    rng = np.random.default_rng(cfg.seed)
+    lay = W.gen_layout(cfg, rng)
+    n = cfg.B * cfg.T
+    maxc = int(lay.ctx.max())
+    ps = M.INDEX_PAGE_BYTES
+    t0 = time.time()
+    pool = torch.zeros(lay.num_pages * ps, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    for b in range(cfg.B):  # every position of every request, keys N(0,1)
+        L = int(lay.ctx[b])
+        slots = torch.from_numpy(W.slots_for_request(lay, b, np.arange(L))).to(dev)
+        keys = torch.randn((L, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        M.mla_index_key_quant(keys, slots, pool, ps, lay.num_pages)
+    torch.cuda.synchronize()
+    log(f"[bench] index logits: {n} query tokens, HI={HI}, contexts up to {maxc}, pool {pool.numel() / 1e9:.2f} GB "
+        f"({time.time() - t0:.1f} s)")
+    bt = torch.from_numpy(lay.block_table).to(dev)
+    ctx = torch.from_numpy(lay.ctx).to(dev)
+    q_sets = [torch.randn((cfg.B, cfg.T, HI, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(N_SETS)]
+    w_sets = [torch.randn((cfg.B, cfg.T, HI), generator=gen, device=dev) / HI ** 0.5 for _ in range(N_SETS)]
+    out = torch.empty((n, (maxc + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.mla_index_logits(q_sets[i % N_SETS], w_sets[i % N_SETS], pool, ps, lay.num_pages, bt, ctx, maxc,
+                           causal=cfg.causal, out=out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    call_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    call_avg = float(np.mean(call_us))
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step; call avg {call_avg:.2f} us, "
+        f"p10 {np.percentile(call_us, 10):.2f}, p90 {np.percentile(call_us, 90):.2f}")
+    # algorithmic work: each request's keys (128 code bytes + a 4-byte scale per position) read once, the
+    # query tokens' q and w read, one fp32 logit written per (query token, visible position)
+    visible = sum(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1 for b in range(cfg.B) for t in range(cfg.T))
+    bytes_per = int(int(lay.ctx.astype(np.int64).sum()) * 132 + n * HI * (128 * 2 + 4) + visible * 4)
+    flops = 2.0 * HI * 128 * visible
+    ach = bytes_per / (call_avg * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "mla_index_logits call: index_logits_kernel<%d>, timed with HIP events on its stream" % HI,
+            "algorithmic_bytes_per_launch": bytes_per, "flops_per_launch": flops,
+            "mfma_tflops": round(flops / (call_avg * 1e-6) / 1e12, 1), "launch_us": round(call_avg, 3)}
+    res = {
+        "metric": "indexer logits query-tokens/s (FP8 keys of each context, %d index heads); %% of roofline" % HI,
+        "value": round(n / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "index_heads": HI,
+                   "context": cfg.ctx or list(cfg.ctx_range), "causal": cfg.causal, "key_bytes": 132,
+                   "step": "index logits"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle over the first few requests (a bounded sample, one query-token group per host thread):
+        # their pool pages copied out and renumbered
+        nthreads = len(os.sched_getaffinity(0))
+        S = max(1, min(cfg.B, nthreads, 16))
+        pages = [lay.block_table[b][lay.block_table[b] >= 0] for b in range(S)]
+        allp = np.concatenate(pages).astype(np.int64)
+        host = pool.view(-1, ps)[torch.from_numpy(allp).to(dev)].cpu().numpy().reshape(-1)
+        bt1 = np.full((S, max(p.size for p in pages)), -1, np.int32)
+        off = 0
+        for b in range(S):
+            bt1[b, :pages[b].size] = np.arange(off, off + pages[b].size)
+            off += pages[b].size
+        q1 = q_sets[0][:S].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        w1 = w_sets[0][:S].contiguous().cpu().numpy()
+        times, used = [], 1
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.index_logits(q1, w1, host, ps, off, bt1, lay.ctx[:S], causal=cfg.causal, nthreads=nthreads)
+            times.append(time.perf_counter() - t0)
+        used = min(nthreads, S * cfg.T)
+        tmed = float(np.median(times))
+        res["cpu_baseline"] = {"value": round(S * cfg.T / tmed, 3), "unit": "query-tokens/s", "cores": used,
+                               "kind": "oracle", "sample": f"{S * cfg.T} of {n} query tokens (requests 0..{S - 1}), "
+                                                           f"median of 3 runs of {tmed:.2f} s on {used} threads"}
     print(json.dumps(res), flush=True)
 
 

@@ -184,6 +184,47 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
                         void* stream);
 
 /*
+ * Sparse-indexer keys (analysis page, section "Four bits per latent value: where 352 comes from": 128 FP8
+ * values plus a scale per token, stored the way DeepSeek's indexer is; the pages give no quantization
+ * rule, and this one is the TokenSpeed write-up's per-token FP8 rule from its MLA KV layout section):
+ * for each key r, with x = keys[r*key_stride .. +127] (bf16), in fp32:
+ *     s = max(max_i |x_i|, 1e-26) / 448,  code_i = E4M3(x_i / s) (nearest, ties to even, saturating,
+ *     sign from x_i),
+ * written to indexer-pool page slot/64, row slot%64: the 128 codes at page + (slot%64)*128 and s at
+ * page + 8192 + (slot%64)*4 (a page is 64 code rows, then 64 fp32 scales: 8448 bytes).
+ *   keys               (device) bf16, 4-byte aligned, key_stride >= 128 elements and even
+ *   slot_mapping       (device) int64 [n], 8-byte aligned; negative slots and slots on pages outside
+ *                      [0, num_pages) are skipped
+ *   pool               (device) 16-byte aligned, page p at pool + p*page_stride_bytes
+ *   page_stride_bytes  >= 8448, a multiple of 16
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (n < 0, num_pages < 1), MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_index_key_quant(const void* keys, int64_t key_stride, const int64_t* slot_mapping, int64_t n, void* pool,
+                        int64_t page_stride_bytes, int64_t num_pages, void* stream);
+
+/*
+ * Sparse-indexer logits.  No page defines them; this is the DeepSeek-style form that the analysis page
+ * points to.  For query token id = b*T + t and every position p <= limit (limit as for mla_sparse_decode):
+ *     logits[id*ld + p] = s_p * sum_j w[id*HI + j] * max(0, <q[id][j][:], k_p>)
+ * k_p = the E4M3 values of position p's key (through the request's page table), s_p its scale; the dot
+ * products are exact products accumulated in fp32 (bf16 MFMA), the head sum in fp32.  Positions whose
+ * page entry is outside [0, num_pages) get -inf; positions past the limit are not written.
+ *   q             (device) bf16 [B, T, HI, 128] contiguous, 16-byte aligned
+ *   w             (device) fp32 [B, T, HI], 16-byte aligned (per-head weights, the softmax scale included)
+ *   HI            16, 32 or 64 index heads
+ *   pool, page_stride_bytes, num_pages   the indexer pool as written by mla_index_key_quant
+ *   block_table, bt_stride, context_lens, B, T, causal   as for mla_sparse_decode (shared with the MLA cache)
+ *   max_context   >= every context_lens[b] (it sizes the grid)
+ *   logits        (device) fp32 [B*T, ld], 4-byte aligned, ld >= max_context; feed it to mla_index_topk with
+ *                 lengths limit + 1
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_index_logits(const void* q, const float* w, int32_t HI, const void* pool, int64_t page_stride_bytes,
+                     int64_t num_pages, const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                     int32_t B, int32_t T, int32_t max_context, int32_t causal, float* logits, int64_t ld,
+                     void* stream);
+
+/*
  * Index top-k: the sparse indexer's selection step that produces the decoders' index lists (launch post:
  * a query token attends to at most 2,048 cached positions picked by the indexer, unused entries -1; the
  * analysis page, section "Decode: TP4, and the copies it keeps": index_topk 2048).  The pages do not define the

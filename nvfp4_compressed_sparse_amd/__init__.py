@@ -23,8 +23,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_index_topk_workspace_bytes",
-    "mla_index_topk",
+    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_index_key_quant", "mla_index_logits",
+    "mla_index_topk_workspace_bytes", "mla_index_topk",
 ]
 
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
         "mla_stage_nvfp4_fp8": (ctypes.c_int, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, P, P, P, P]),
+        "mla_index_key_quant": (ctypes.c_int, [P, i64, P, i64, P, i64, i64, P]),
+        "mla_index_logits": (ctypes.c_int, [P, P, i32, P, i64, i64, P, i64, P, i32, i32, i32, i32, P, i64, P]),
         "mla_index_topk_workspace_bytes": (sz, [i64, i64]),
         "mla_index_topk": (ctypes.c_int, [P, i64, P, i64, i32, P, P, sz, P]),
     }
@@ -251,6 +253,63 @@ def mla_stage_nvfp4_fp8(pool, page_stride_bytes, num_pages, block_table, context
                                    staged_lens.data_ptr(), _stream(stream))
     _check("mla_stage_nvfp4_fp8", st)
     return staged, staged_block_table, staged_lens
+
+
+# --------------------------------------------------------------------------- sparse-indexer keys and logits
+INDEX_DIM, INDEX_PAGE_BYTES = 128, 64 * 128 + 64 * 4
+
+
+def mla_index_key_quant(keys, slot_mapping, pool, page_stride_bytes, num_pages, stream=None):
+    """Write n indexer keys (bf16 [n, 128], unit inner stride) as 128 E4M3 codes + an fp32 scale each into
+    the paged indexer pool (see include/mla_nvfp4.h)."""
+    import torch
+    _dev(keys, torch.bfloat16, "keys")
+    _dev(slot_mapping, torch.int64, "slot_mapping")
+    _dev(pool, torch.uint8, "pool")
+    n = slot_mapping.numel()
+    if keys.dim() != 2 or keys.shape[1] != INDEX_DIM or keys.stride(1) != 1 or keys.shape[0] != n:
+        raise ValueError("keys must be [n, 128] with unit inner stride")
+    if not slot_mapping.is_contiguous() or not pool.is_contiguous():
+        raise ValueError("slot_mapping and pool must be contiguous")
+    if num_pages < 1 or pool.numel() < page_stride_bytes * (num_pages - 1) + INDEX_PAGE_BYTES:
+        raise ValueError("pool too small for num_pages pages of page_stride_bytes")
+    st = lib().mla_index_key_quant(keys.data_ptr(), keys.stride(0), slot_mapping.data_ptr(), n, pool.data_ptr(),
+                                   int(page_stride_bytes), int(num_pages), _stream(stream))
+    _check("mla_index_key_quant", st)
+
+
+def mla_index_logits(q, w, pool, page_stride_bytes, num_pages, block_table, context_lens, max_context, causal=False,
+                     out=None, stream=None):
+    """Indexer logits (a DeepSeek-style reading; see include/mla_nvfp4.h): q bf16 [B, T, HI, 128], w fp32
+    [B, T, HI].  Returns fp32 [B*T, ld] (ld = max_context rounded up to 4; positions past each query
+    token's limit are left as allocated)."""
+    import torch
+    _dev(q, torch.bfloat16, "q")
+    _dev(w, torch.float32, "w")
+    _dev(pool, torch.uint8, "pool")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(context_lens, torch.int32, "context_lens")
+    if q.dim() != 4 or q.shape[3] != INDEX_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, T, HI, 128] tensor")
+    B, T, HI, _ = q.shape
+    if tuple(w.shape) != (B, T, HI) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [B, T, HI] tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, pages] tensor")
+    if context_lens.numel() != B or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] tensor")
+    ld = (int(max_context) + 3) // 4 * 4
+    if out is None:
+        out = torch.empty((B * T, ld), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out")
+    if out.dim() != 2 or out.shape[0] != B * T or out.shape[1] < max_context or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B*T, >= max_context] tensor")
+    st = lib().mla_index_logits(q.data_ptr(), w.data_ptr(), HI, pool.data_ptr(), int(page_stride_bytes),
+                                int(num_pages), block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
+                                B, T, int(max_context), int(bool(causal)), out.data_ptr(), out.shape[1],
+                                _stream(stream))
+    _check("mla_index_logits", st)
+    return out
 
 
 # --------------------------------------------------------------------------- index top-k

@@ -212,3 +212,42 @@ def test_index_topk_workspace_size():
         want = r256(n * 4096 * 4) + r256(n * 32) + r256(n * chunks * 8) + r256(n * 8192 * 8)
         assert M.lib().mla_index_topk_workspace_bytes(n, ld) == want, (n, ld)
     assert M.lib().mla_index_topk_workspace_bytes(0, 4096) == 0
+
+
+def test_index_key_quant_argument_errors():
+    def call(**kw):
+        a = dict(keys=FAKE, ks=128, sm=FAKE, n=10, pool=FAKE, ps=8448, npg=4)
+        a.update(kw)
+        return M.lib().mla_index_key_quant(a["keys"], a["ks"], a["sm"], a["n"], a["pool"], a["ps"], a["npg"], None)
+    for name in ("keys", "sm", "pool"):
+        assert call(**{name: None}) == 1, name
+    assert call(n=-1) == 2
+    assert call(n=0, keys=None, sm=None, pool=None) == 0
+    assert call(npg=0) == 2
+    assert call(ks=127) == 3 and call(ks=129) == 3
+    assert call(ps=8448 - 16) == 3 and call(ps=8448 + 8) == 3
+    assert call(keys=FAKE + 2) == 3 and call(sm=FAKE + 4) == 3 and call(pool=FAKE + 8) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == 5
+
+
+def test_index_logits_argument_errors():
+    def call(**kw):
+        a = dict(q=FAKE, w=FAKE, HI=64, pool=FAKE, ps=8448, npg=4, bt=FAKE, bts=4, ctx=FAKE, B=2, T=1, maxc=256,
+                 causal=0, out=FAKE, ld=256)
+        a.update(kw)
+        return M.lib().mla_index_logits(a["q"], a["w"], a["HI"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"],
+                                        a["ctx"], a["B"], a["T"], a["maxc"], a["causal"], a["out"], a["ld"], None)
+    for name in ("q", "w", "pool", "bt", "ctx", "out"):
+        assert call(**{name: None}) == 1, name
+    for HI in (0, 8, 48, 128):
+        assert call(HI=HI) == 2
+    assert call(B=0) == 2 and call(T=0) == 2 and call(maxc=0) == 2 and call(npg=0) == 2 and call(bts=0) == 2
+    assert call(causal=2) == 2
+    assert call(ld=255) == 2
+    assert call(ps=8432) == 3 and call(ps=8456) == 3
+    assert call(q=FAKE + 8) == 3 and call(w=FAKE + 4) == 3 and call(out=FAKE + 2) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == 5

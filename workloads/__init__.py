@@ -20,6 +20,9 @@ these inputs stand in for it with the pages' shapes):
     "ties" integers 0..3 (bins far larger than the candidate buffer); "equal" all 0.5; "special" a mix
     of -0.0, +0.0, +-inf, subnormals, +-FLT_MAX and N(0,1); "ramp" N(0,1) + 6 * position / ld (the
     largest values crowd into the last positions, as a recency trend would put them).
+  * sparse-indexer inputs (the pages give the key size only): keys N(0,1) -> bf16 [tokens, 128]; index
+    queries N(0,1) -> bf16 [B, T, HI, 128]; head weights N(0,1) * HI^-1/2, fp32 [B, T, HI]; the
+    indexer pool uses the MLA cache's page table.
 CPU generators use numpy PCG64; device generators use a seeded torch generator on the GPU.
 """
 from __future__ import annotations
@@ -294,3 +297,19 @@ def gen_logits(rng: np.random.Generator, n: int, ld: int, kind: str = "normal") 
         x = rng.standard_normal((n, ld), dtype=np.float32)
         return x + (np.float32(6.0) * np.arange(ld, dtype=np.float32) / np.float32(ld))[None, :]
     raise ValueError(kind)
+
+
+# --------------------------------------------------------------------------- sparse-indexer inputs
+INDEX_DIM = 128
+
+
+def gen_index_keys(rng: np.random.Generator, n: int) -> np.ndarray:
+    """bf16 bits [n, 128] of N(0,1) indexer keys."""
+    return bf16_bits(rng.standard_normal((n, INDEX_DIM)).astype(np.float32))
+
+
+def gen_index_query(rng: np.random.Generator, B: int, T: int, HI: int):
+    """(q bf16 bits [B, T, HI, 128], w float32 [B, T, HI])."""
+    q = bf16_bits(rng.standard_normal((B, T, HI, INDEX_DIM)).astype(np.float32))
+    w = (rng.standard_normal((B, T, HI)) / math.sqrt(HI)).astype(np.float32)
+    return q, w
