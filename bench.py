@@ -366,8 +366,8 @@ def bench_index_topk(args):
     ach = bytes_per / (call_avg * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "mla_index_topk call: topk_hist_kernel, topk_collect_kernel, topk_finish_kernel, timed with HIP events "
-                      "on their stream",
+            "kernel": "mla_index_topk call: topk_hist_kernel, topk_collect_kernel, topk_finish_kernel, timed with "
+                      "HIP events on their stream",
             "algorithmic_bytes_per_launch": bytes_per, "launch_us": round(call_avg, 3)}
     res = {
         "metric": "index top-k query-tokens/s (fp32 logits over each context, top-%d); %% of roofline" % cfg.topk,
@@ -466,7 +466,8 @@ def bench_index_logits(args):
         f"p10 {np.percentile(call_us, 10):.2f}, p90 {np.percentile(call_us, 90):.2f}")
     # algorithmic work: each request's keys (128 code bytes + a 4-byte scale per position) read once, the
     # query tokens' q and w read, one fp32 logit written per (query token, visible position)
-    visible = sum(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1 for b in range(cfg.B) for t in range(cfg.T))
+    visible = sum(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1
+                  for b in range(cfg.B) for t in range(cfg.T))
     bytes_per = int(int(lay.ctx.astype(np.int64).sum()) * 132 + n * HI * (128 * 2 + 4) + visible * 4)
     flops = 2.0 * HI * 128 * visible
     ach = bytes_per / (call_avg * 1e-6) / 1e9

@@ -26,7 +26,7 @@
 // of the page, scaled by s_p.  Positions past the query token's limit are not written; positions on a
 // page-table entry outside the pool get -inf.
 #include "mla_device.h"
-#include "mla_internal.h"
+#include "mla_index_internal.h"
 
 namespace mla {
 
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void index_logits_kernel(IndexLogitsArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        qf[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qt + (16 * mt + r16) * kIdxDim + 32 * g + 8 * ks));
+        qf[mt][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(qt + (16 * mt + r16) * kIdxDim + 32 * g + 8 * ks));
     f32x4 wv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) wv[mt] = *reinterpret_cast<const f32x4*>(a.w + id * HI + 16 * mt + 4 * g);

@@ -18,7 +18,7 @@
 //     plus the first ties by position, a block scan giving each its output slot.  When the candidates
 //     do not fit (very many equal or near-equal logits), it runs the same steps over the whole row.  It
 //     also returns the row's histogram and counters to zero for the next call.
-#include "mla_internal.h"
+#include "mla_index_internal.h"
 
 namespace mla {
 
