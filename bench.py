@@ -111,10 +111,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
-    ap.add_argument("--op", default="decode", choices=["decode", "index-topk", "index-logits"],
+    ap.add_argument("--op", default="decode", choices=["decode", "index-topk", "index-logits", "dsa-step"],
                     help="decode: the decode step (default); index-topk: the indexer's top-k selection over fp32 "
                          "logits of the workload's query tokens and contexts; index-logits: the indexer's logits "
-                         "over FP8 keys (a DeepSeek-style reading)")
+                         "over FP8 keys (a DeepSeek-style reading); dsa-step: indexer logits, top-k and the sparse "
+                         "decode in sequence, each timed")
     ap.add_argument("--index-heads", type=int, default=64, help="index-logits: index heads (16, 32 or 64)")
     ap.add_argument("--logits", default="normal", choices=["normal", "ramp"],
                     help="index-topk: N(0,1) logits, or N(0,1) plus a rising trend over positions")
@@ -132,6 +133,9 @@ def main():
         return
     if args.op == "index-logits":
         bench_index_logits(args)
+        return
+    if args.op == "dsa-step":
+        bench_dsa_step(args)
         return
 
     import torch
@@ -521,6 +525,105 @@ def bench_index_logits(args):
         res["cpu_baseline"] = {"value": round(S * cfg.T / tmed, 3), "unit": "query-tokens/s", "cores": used,
                                "kind": "oracle", "sample": f"{S * cfg.T} of {n} query tokens (requests 0..{S - 1}), "
                                                            f"median of 3 runs of {tmed:.2f} s on {used} threads"}
+    print(json.dumps(res), flush=True)
+
+
+def bench_dsa_step(args):
+    """A whole sparse decode step on one layer: indexer logits over each query token's context, the
+    top-k of them, then the NVFP4 sparse decode over the chosen rows (the new rows' quantize-on-write
+    included), each stage timed with HIP events on the one stream."""
+    import torch
+    import nvfp4_compressed_sparse_amd as M
+
+    cfg = W.CONFIGS[args.workload]
+    if not (cfg.topk and cfg.fmt == "nvfp4"):
+        raise SystemExit("--op dsa-step applies to the sparse NVFP4 workloads")
+    HI = args.index_heads
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = W.device_inputs(cfg, dev, n_sets=2)
+    lay = inp["layout"]
+    pool = torch.zeros(lay.num_pages * cfg.page_stride, dtype=torch.uint8, device=dev)
+    M.mla_kv_quant_nvfp4(inp["lat"], inp["rope"], inp["slots"], pool, cfg.page_stride, lay.num_pages)
+    rows = torch.from_numpy(np.concatenate([inp["row_off"][b] + lay.ctx[b] - cfg.T + np.arange(cfg.T)
+                                            for b in range(cfg.B)]).astype(np.int64)).to(dev)
+    w_lat, w_rope, w_slots = inp["lat"][rows].contiguous(), inp["rope"][rows].contiguous(), inp["slots"][rows]
+    del inp["lat"], inp["rope"]
+    ips = M.INDEX_PAGE_BYTES
+    ipool = torch.zeros(lay.num_pages * ips, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 1)
+    keys = torch.randn((inp["slots"].numel(), 128), generator=gen, device=dev).to(torch.bfloat16)
+    M.mla_index_key_quant(keys, inp["slots"], ipool, ips, lay.num_pages)
+    del keys
+    torch.cuda.synchronize()
+    n, maxc = cfg.B * cfg.T, int(lay.ctx.max())
+    lens = torch.from_numpy(np.array([W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1
+                                      for b in range(cfg.B) for t in range(cfg.T)], np.int32)).to(dev)
+    qi = [torch.randn((cfg.B, cfg.T, HI, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+    wi = [torch.randn((cfg.B, cfg.T, HI), generator=gen, device=dev) / HI ** 0.5 for _ in range(2)]
+    logits = torch.empty((n, (maxc + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    tk_ws = torch.zeros(M.mla_index_topk_workspace_bytes(n, logits.shape[1]), dtype=torch.uint8, device=dev)
+    idx = torch.empty((cfg.B, cfg.T, cfg.topk), dtype=torch.int32, device=dev)
+    S = M.mla_sparse_decode_splits(cfg.B, cfg.T, cfg.H, cfg.topk)
+    ws = torch.zeros(max(M.mla_sparse_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S), 256),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.B, cfg.T, cfg.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        k = i % 2
+        if ev is not None:
+            ev[0].record(stream)
+        M.mla_index_logits(qi[k], wi[k], ipool, ips, lay.num_pages, inp["bt"], inp["ctx"], maxc, causal=cfg.causal,
+                           out=logits, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.mla_index_topk(logits, lens, cfg.topk, out=idx.view(n, cfg.topk), workspace=tk_ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        M.mla_kv_quant_nvfp4(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
+        M.mla_sparse_decode(inp["q_sets"][k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx,
+                            cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    stage = [float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])) for j in range(3)]
+    log(f"[bench] dsa step: {ms_per_step * 1e3:.1f} us/step; logits {stage[0]:.1f}, top-k {stage[1]:.1f}, "
+        f"write + decode {stage[2]:.1f} us")
+    res = {
+        "metric": "sparse decode step (indexer logits + top-k + NVFP4 sparse-MLA decode) query-tokens/s",
+        "value": round(n / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "H": cfg.H, "index_heads": HI,
+                   "topk": cfg.topk, "context": cfg.ctx or list(cfg.ctx_range), "splits": S,
+                   "step": "index logits + top-k + quantize %d rows + decode" % n},
+        "stages_us": {"index_logits": round(stage[0], 2), "index_topk": round(stage[1], 2),
+                      "write_and_decode": round(stage[2], 2)},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
 
 
