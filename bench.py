@@ -125,7 +125,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in DESIGN.md "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the sharding across GPUs is a design note, "
                                    "but not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.op == "index-topk":
