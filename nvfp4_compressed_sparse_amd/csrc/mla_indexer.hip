@@ -32,6 +32,7 @@ namespace mla {
 
 constexpr int kIdxDim = 128;
 constexpr int kIdxCodes = 64 * kIdxDim;  // scales follow the page's code rows
+constexpr size_t kIdxMultiMaxLds = 72 * 1024;  // q and w of the request's tokens, for T > 1
 
 __global__ __launch_bounds__(256) void index_key_quant_kernel(IndexKeyArgs a) {
   const int lane = threadIdx.x & 63;
@@ -156,13 +157,110 @@ __global__ __launch_bounds__(256) void index_logits_kernel(IndexLogitsArgs a) {
   }
 }
 
+// Several query tokens per request (T > 1): each page's keys are read and converted once and used for
+// every token.  q and w of the request's T tokens sit in LDS (q rows padded to 272 bytes so that the 16
+// rows a load instruction touches spread over the banks); per page the wave converts its keys to bf16 once,
+// then for each token and head tile reads the q fragments from LDS.  One page of keys in flight.
+constexpr int kQRowBytes = kIdxDim * 2 + 16;
+
+template <int HI>
+__global__ __launch_bounds__(256) void index_logits_multi_kernel(IndexLogitsArgs a) {
+  constexpr int MT = HI / 16;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int b = blockIdx.x / a.chunks;
+  const int T = a.T;
+  float* wl = reinterpret_cast<float*>(lds + T * HI * kQRowBytes);
+  {  // the request's q (T*HI rows of 256 bytes, 16 per thread-load) and w into LDS
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * T * HI * kIdxDim);
+    for (int c = tid; c < T * HI * 16; c += 256) {
+      const int row = c >> 4, off = (c & 15) * 16;
+      *reinterpret_cast<u32x4*>(lds + row * kQRowBytes + off) = *reinterpret_cast<const u32x4*>(qsrc + row * 256 + off);
+    }
+    for (int c = tid; c < T * HI; c += 256) wl[c] = a.w[(int64_t)b * T * HI + c];
+  }
+  __syncthreads();
+  const int pg_first = (blockIdx.x % a.chunks) * kIdxPagesPerWg + (tid >> 6) * kIdxPagesPerWave;
+  const int L = a.ctx[b];
+  const int p_end = L < a.ld ? L : (int)a.ld;
+  if (pg_first * 64 >= p_end) return;
+  const int n_pages = min(kIdxPagesPerWave, (p_end - pg_first * 64 + 63) / 64);
+  auto page_base = [&](int pg, bool& ok) -> const uint8_t* {
+    const int64_t phys = pg < a.bt_stride ? a.block_table[(int64_t)b * a.bt_stride + pg] : -1;
+    ok = phys >= 0 && phys < a.num_pages;
+    return a.pool + (ok ? phys : 0) * a.page_stride;
+  };
+
+  IndexPage buf[2];
+  bool ok[2];
+  load_index_page(page_base(pg_first, ok[0]), r16, g, lane, buf[0]);
+#pragma unroll
+  for (int i = 0; i < kIdxPagesPerWave; ++i) {
+    if (i >= n_pages) break;
+    if (i + 1 < kIdxPagesPerWave)
+      load_index_page(page_base(pg_first + (i + 1 < n_pages ? i + 1 : i), ok[(i + 1) % 2]), r16, g, lane,
+                      buf[(i + 1) % 2]);
+    const IndexPage& cur = buf[i % 2];
+    bf16x8 kf[4][4];  // tile nt, k-step ks: key bytes 8ks..8ks+7 of the lane's 32
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      kf[nt][0] = e4m3x8_to_bf16x8(cur.k[nt][0][0], cur.k[nt][0][1]);
+      kf[nt][1] = e4m3x8_to_bf16x8(cur.k[nt][0][2], cur.k[nt][0][3]);
+      kf[nt][2] = e4m3x8_to_bf16x8(cur.k[nt][1][0], cur.k[nt][1][1]);
+      kf[nt][3] = e4m3x8_to_bf16x8(cur.k[nt][1][2], cur.k[nt][1][3]);
+    }
+    const int p = (pg_first + i) * 64 + lane;
+    for (int t = 0; t < T; ++t) {
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t* qrow = lds + (t * HI + 16 * mt + r16) * kQRowBytes + 64 * g;
+        bf16x8 qf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks));
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(wl + t * HI + 16 * mt + 4 * g);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(qf[ks], kf[nt][ks], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[nt] += wv[e] * fmaxf(acc[e], 0.0f);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        part[nt] += __shfl_xor(part[nt], 16, 64);
+        part[nt] += __shfl_xor(part[nt], 32, 64);
+      }
+      const float mine = g == 0 ? part[0] : (g == 1 ? part[1] : (g == 2 ? part[2] : part[3]));
+      const int lim = a.causal ? L - T + t : L - 1;
+      if (p <= lim && p < p_end)
+        a.logits[((int64_t)b * T + t) * a.ld + p] = ok[i % 2] ? mine * cur.sc : -INFINITY;
+    }
+  }
+}
+
 hipError_t launch_index_key_quant(const IndexKeyArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(index_key_quant_kernel, dim3((unsigned)((a.n + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+size_t index_logits_multi_lds(int T, int HI) { return (size_t)T * HI * (kQRowBytes + 4); }
+
 hipError_t launch_index_logits(const IndexLogitsArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.B * a.chunks)), block(256);
+  if (a.T > 1 && index_logits_multi_lds(a.T, a.HI) <= kIdxMultiMaxLds) {
+    const size_t lds = index_logits_multi_lds(a.T, a.HI);
+    switch (a.HI) {
+      case 16: hipLaunchKernelGGL(index_logits_multi_kernel<16>, grid, block, lds, stream, a); break;
+      case 32: hipLaunchKernelGGL(index_logits_multi_kernel<32>, grid, block, lds, stream, a); break;
+      case 64: hipLaunchKernelGGL(index_logits_multi_kernel<64>, grid, block, lds, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.HI) {
     case 16: hipLaunchKernelGGL(index_logits_kernel<16>, grid, block, 0, stream, a); break;
     case 32: hipLaunchKernelGGL(index_logits_kernel<32>, grid, block, 0, stream, a); break;
