@@ -13,7 +13,9 @@
 // index_key_quant_kernel: one wave per key, lane l holds values 2l and 2l+1; the amax is a wave
 // maximum; each lane writes its two code bytes, lane 0 the scale.
 //
-// index_logits_kernel: each wave takes kIdxPagesPerWave consecutive 64-position pages of a request (four
+// index_logits_kernel (used when a request's q does not fit the LDS budget of index_logits_multi_kernel,
+// which otherwise serves every T and is described below): each wave takes kIdxPagesPerWave consecutive
+// 64-position pages of a request (four
 // waves per workgroup).  For each query token of the request the wave loads q once and walks its pages,
 // the next two pages' keys in flight while it computes S = Q K^T for all index heads with bf16 MFMA
 // 16x16x32:
@@ -157,10 +159,12 @@ __global__ __launch_bounds__(256) void index_logits_kernel(IndexLogitsArgs a) {
   }
 }
 
-// Several query tokens per request (T > 1): each page's keys are read and converted once and used for
-// every token.  q and w of the request's T tokens sit in LDS (q rows padded to 272 bytes so that the 16
-// rows a load instruction touches spread over the banks); per page the wave converts its keys to bf16 once,
-// then for each token and head tile reads the q fragments from LDS.  One page of keys in flight.
+// The kernel used whenever q and w of a request's T tokens fit kIdxMultiMaxLds of LDS (T * HI <= 256):
+// each page's keys are read and converted once and used for every token.  q and w sit in LDS (q rows
+// padded to 272 bytes so that the 16 rows a load instruction touches spread over the banks); per page the
+// wave converts its keys to bf16 once, then for each token and head tile reads the q fragments from LDS.
+// One page of keys in flight; 150 VGPRs, three waves per SIMD (the register-q kernel above needs 231 and
+// runs two; at one token it is 3% slower).
 constexpr int kQRowBytes = kIdxDim * 2 + 16;
 
 template <int HI>
@@ -251,7 +255,7 @@ size_t index_logits_multi_lds(int T, int HI) { return (size_t)T * HI * (kQRowByt
 
 hipError_t launch_index_logits(const IndexLogitsArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.B * a.chunks)), block(256);
-  if (a.T > 1 && index_logits_multi_lds(a.T, a.HI) <= kIdxMultiMaxLds) {
+  if (index_logits_multi_lds(a.T, a.HI) <= kIdxMultiMaxLds) {
     const size_t lds = index_logits_multi_lds(a.T, a.HI);
     switch (a.HI) {
       case 16: hipLaunchKernelGGL(index_logits_multi_kernel<16>, grid, block, lds, stream, a); break;
