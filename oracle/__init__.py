@@ -59,6 +59,10 @@ def _load():
         "mlo_scale_code_bulk": (None, [P, i64, P]),
         "mlo_quant_row_nvfp4": (None, [P, P, P]),
         "mlo_index_key_quant_row": (None, [P, P, P]),
+        "mlo_pth_quant_row": (None, [P, P, P, P, P]),
+        "mlo_kv_quant_pth": (i64, [P, i64, P, i64, P, i64, P, P, P, i64]),
+        "mlo_dequant_row_pth": (None, [P, ctypes.c_float, P, P]),
+        "mlo_sparse_decode_pth": (i32, [P, P, P, P, i64, P, i64, P, P, i32, i32, i32, i32, d, i32, P, i64, P, P, i32]),
         "mlo_index_key_quant": (i64, [P, i64, P, i64, P, i64, i64]),
         "mlo_index_logits": (i32, [P, P, i32, P, i64, i64, P, i64, P, i32, i32, i32, P, i64, i32]),
         "mlo_quant_row_fp8": (None, [P, P, P]),
@@ -255,6 +259,66 @@ def stage_nvfp4_fp8(pool, page_stride, num_pages, block_table, ctx, indices, cau
     _load().mlo_stage_nvfp4_fp8(_ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T,
                                 k, int(bool(causal)), R, _ptr(staged), _ptr(counts))
     return staged, counts
+
+
+# --------------------------------------------------------------------------- per-token-head FP8 layout
+
+def kv_quant_pth(k_nope, k_rope, slot_mapping, lat_buf, scale_buf, rope_buf):
+    """TokenSpeed's per-token-head FP8 write (its MLA KV layout section): latent codes uint8 [slots, 512],
+    fp32 scales [slots], bf16-bit rope [slots, 64], modified in place.  Returns the number written."""
+    kn = np.ascontiguousarray(k_nope, dtype=np.uint16)
+    kr = np.ascontiguousarray(k_rope, dtype=np.uint16)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    n = sm.size
+    assert kn.shape == (n, LATENT) and kr.shape == (n, ROPE)
+    slots = scale_buf.size
+    assert lat_buf.dtype == np.uint8 and lat_buf.shape == (slots, LATENT) and lat_buf.flags.c_contiguous
+    assert scale_buf.dtype == np.float32 and rope_buf.dtype == np.uint16 and rope_buf.shape == (slots, ROPE)
+    return _load().mlo_kv_quant_pth(_ptr(kn), LATENT, _ptr(kr), ROPE, _ptr(sm), n, _ptr(lat_buf), _ptr(scale_buf),
+                                    _ptr(rope_buf), slots)
+
+
+def pth_quant_row(lat, rope):
+    """One token: (codes uint8 [512], scale float, rope bf16 bits [64])."""
+    lv = np.ascontiguousarray(lat, dtype=np.uint16)
+    rv = np.ascontiguousarray(rope, dtype=np.uint16)
+    codes = np.zeros(LATENT, np.uint8)
+    sc = np.zeros(1, np.float32)
+    rq = np.zeros(ROPE, np.uint16)
+    _load().mlo_pth_quant_row(_ptr(lv), _ptr(rv), _ptr(codes), _ptr(sc), _ptr(rq))
+    return codes, float(sc[0]), rq
+
+
+def dequant_row_pth(codes, scale, rq):
+    """K[576] (float64) of one per-token-head slot: code values x scale, stored rope x scale."""
+    K = np.zeros(QK, np.float64)
+    _load().mlo_dequant_row_pth(_ptr(np.ascontiguousarray(codes, np.uint8)), ctypes.c_float(scale),
+                                _ptr(np.ascontiguousarray(rq, np.uint16)), _ptr(K))
+    return K
+
+
+def sparse_decode_pth(q, lat_buf, scale_buf, rope_buf, block_table, ctx, indices, sm_scale, causal=False, units=None,
+                      nthreads=0):
+    """Sparse decode over the per-token-head layout (same selection rule as sparse_decode; slot =
+    page*64 + position%64).  Returns (out float64 [B,T,H,512] or [n_units,H,512], lse, threads used)."""
+    qv = np.ascontiguousarray(q, dtype=np.uint16)
+    B, T, H, _ = qv.shape
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    k = idx.shape[2]
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cx = np.ascontiguousarray(ctx, dtype=np.int32)
+    un = None if units is None else np.ascontiguousarray(units, dtype=np.int64)
+    nq = B * T if un is None else un.size
+    out = np.zeros((nq, H, LATENT), np.float64)
+    lse = np.zeros((nq, H), np.float64)
+    used = _load().mlo_sparse_decode_pth(_ptr(qv), _ptr(lat_buf), _ptr(scale_buf), _ptr(rope_buf), scale_buf.size,
+                                         _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T, H, k, float(sm_scale),
+                                         int(bool(causal)), None if un is None else _ptr(un), nq, _ptr(out),
+                                         _ptr(lse), nthreads)
+    if un is None:
+        out = out.reshape(B, T, H, LATENT)
+        lse = lse.reshape(B, T, H)
+    return out, lse, used
 
 
 # --------------------------------------------------------------------------- sparse indexer keys and logits

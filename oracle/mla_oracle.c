@@ -30,6 +30,12 @@
  *    ignored (as if absent); an empty selection gives out = 0 and lse = -inf;
  *  - duplicates count once per occurrence (plain multiset softmax).
  *
+ * Per-token-head FP8 layout (TokenSpeed write-up, MLA KV layout section): three slot-indexed buffers,
+ * latent codes [slots, 512] E4M3, one fp32 scale per slot, rope [slots, 64] in the model dtype (bf16).
+ * The write is the write-up's: in fp32, s = max(amax(latent), 1e-26) / 448, codes = E4M3(x / s),
+ * rope = bf16(r / s).  Readings: E4M3 and bf16 rounding nearest with ties to even (bf16 overflow gives
+ * inf); the read reconstructs K = (code value * s, rope * s), the plain inverse of the write.
+ *
  * Sparse indexer (analysis page, section "Four bits per latent value: where 352 comes from": the
  * indexer keeps 128 FP8 values plus a scale per token on the layers that have one, stored the way
  * DeepSeek's indexer is; the launch post and the analysis page: each query token keeps at most 2,048
@@ -387,6 +393,91 @@ void mlo_stage_nvfp4_fp8(const uint8_t* pool, int64_t page_stride, int64_t num_p
     }
     counts[id] = n;
   }
+}
+
+/* ------------------------------------------------------------------ per-token-head FP8 layout */
+
+/* fp32 -> bf16 bits, nearest with ties to even (finite inputs; values past the largest bf16 give inf). */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* One token: latent bf16 [512] and rope bf16 [64] -> codes [512], scale, rope bf16 [64] (fp32 steps). */
+void mlo_pth_quant_row(const uint16_t* lat, const uint16_t* rope, uint8_t* codes, float* scale, uint16_t* rq) {
+  float amax = 0.0f;
+  for (int i = 0; i < LATENT; ++i) {
+    float v = fabsf((float)mlo_bf16_value(lat[i]));
+    if (v > amax) amax = v;
+  }
+  float s = (amax > 1e-26f ? amax : 1e-26f) / 448.0f;
+  for (int i = 0; i < LATENT; ++i) {
+    float y = (float)mlo_bf16_value(lat[i]) / s;
+    uint32_t sign = (lat[i] >> 15) & 1;
+    codes[i] = (uint8_t)((sign << 7) | nearest_e4m3_code(fabs((double)y), 1.0));
+  }
+  for (int i = 0; i < ROPE; ++i) rq[i] = f32_to_bf16_rne((float)mlo_bf16_value(rope[i]) / s);
+  *scale = s;
+}
+
+/* Write n tokens; token r goes to slot slot_mapping[r] (negative or >= num_slots: skipped).  Strides in
+ * elements. */
+int64_t mlo_kv_quant_pth(const uint16_t* k_nope, int64_t nope_stride, const uint16_t* k_rope, int64_t rope_stride,
+                         const int64_t* slot_mapping, int64_t n, uint8_t* lat_buf, float* scale_buf,
+                         uint16_t* rope_buf, int64_t num_slots) {
+  int64_t written = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t slot = slot_mapping[r];
+    if (slot < 0 || slot >= num_slots) continue;
+    mlo_pth_quant_row(k_nope + r * nope_stride, k_rope + r * rope_stride, lat_buf + slot * LATENT, scale_buf + slot,
+                      rope_buf + slot * ROPE);
+    ++written;
+  }
+  return written;
+}
+
+/* K[576] of one slot: code values times the scale, then the stored rope times the scale. */
+void mlo_dequant_row_pth(const uint8_t* codes, float scale, const uint16_t* rq, double* K) {
+  for (int i = 0; i < LATENT; ++i) K[i] = mlo_e4m3_value(codes[i]) * (double)scale;
+  for (int i = 0; i < ROPE; ++i) K[LATENT + i] = mlo_bf16_value(rq[i]) * (double)scale;
+}
+
+/* Sparse decode over the per-token-head layout: the selection rule of mlo_sparse_decode, with slots
+ * page*64 + position%64 for page entries in [0, num_slots/64). */
+int mlo_sparse_decode_pth(const uint16_t* q, const uint8_t* lat_buf, const float* scale_buf, const uint16_t* rope_buf,
+                          int64_t num_slots, const int32_t* block_table, int64_t bt_stride, const int32_t* ctx,
+                          const int32_t* indices, int B, int T, int H, int topk, double sm_scale, int causal,
+                          const int64_t* units, int64_t n_units, double* out, double* lse, int nthreads) {
+  int used = set_threads(nthreads);
+  int64_t nq = units ? n_units : (int64_t)B * T;
+  int64_t num_pages = num_slots / PAGE;
+#pragma omp parallel
+  {
+    double* K = (double*)malloc(sizeof(double) * QK * (topk > 0 ? topk : 1));
+    double* z = (double*)malloc(sizeof(double) * (topk > 0 ? topk : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < nq; ++u) {
+      int64_t id = units ? units[u] : u;
+      int b = (int)(id / T), t = (int)(id % T);
+      int64_t lim = position_limit(ctx[b], T, t, causal);
+      const int32_t* idx = indices + id * topk;
+      int64_t nrows = 0;
+      for (int j = 0; j < topk; ++j) {
+        int64_t pos = idx[j];
+        if (pos < 0 || pos > lim) continue;
+        int64_t page = block_table[(int64_t)b * bt_stride + pos / PAGE];
+        if (page < 0 || page >= num_pages) continue;
+        int64_t slot = page * PAGE + pos % PAGE;
+        mlo_dequant_row_pth(lat_buf + slot * LATENT, scale_buf[slot], rope_buf + slot * ROPE, K + (nrows++) * QK);
+      }
+      attend(q + id * H * QK, H, K, nrows, sm_scale, out + u * H * LATENT, lse + u * H, z);
+    }
+    free(K);
+    free(z);
+  }
+  return used;
 }
 
 /* ------------------------------------------------------------------ sparse indexer */

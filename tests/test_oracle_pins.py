@@ -755,3 +755,64 @@ def test_index_logits_structure():
     bt_bad = np.array([[0, 7, 2]], np.int32)
     e = oracle.index_logits(q, w1, pool, oracle.INDEX_PAGE_BYTES, 3, bt_bad, [L], causal=True)
     assert np.all(e[:, 64:128] == -np.inf) and np.array_equal(e[:, :64], a[:, :64])
+
+
+# --------------------------------------------------------------------------- per-token-head FP8 layout
+def _bf16_of(x):
+    """bf16 bits of float32 values, nearest with ties to even, computed here independently."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_pth_write_closed_forms():
+    lat = np.zeros(512, np.float32)
+    lat[:3] = [448.0, -3.0, 1.0625]
+    rope = np.zeros(64, np.float32)
+    rope[:2] = [1.5, -2.0]
+    codes, s, rq = oracle.pth_quant_row(_bits(lat), _bits(rope))
+    assert s == 1.0  # amax 448
+    assert list(codes[:3]) == [0x7E, 0xC4, 0x38] and not codes[3:].any()
+    assert list(rq[:2]) == list(_bf16_of([1.5, -2.0])) and not rq[2:].any()
+    # amax 3: the fp32 scale 3/448; the rope is the bf16 of the fp32 quotient r / s
+    lat[:] = 0
+    lat[9] = 3.0
+    rope[:2] = [1.5, 0.1015625]
+    codes, s, rq = oracle.pth_quant_row(_bits(lat), _bits(rope))
+    s32 = np.float32(3.0) / np.float32(448.0)
+    assert s == float(s32) and codes[9] == 0x7E
+    assert list(rq[:2]) == list(_bf16_of(np.array([1.5, 0.1015625], np.float32) / s32))
+    # a near-zero latent: the clamped scale, and a large rope part overflows bf16 to inf
+    lat[:] = 0
+    rope[:2] = [1.0, 2.0 ** 33]
+    codes, s, rq = oracle.pth_quant_row(_bits(lat), _bits(rope))
+    assert s == float(np.float32(1e-26) / np.float32(448.0))
+    assert rq[0] == _bf16_of([np.float32(1.0) / np.float32(s)])[0] and rq[1] == 0x7F80
+
+
+def test_pth_round_trip_and_single_row_decode():
+    rng = np.random.default_rng(62)
+    n = 3
+    lat = _bits((rng.standard_normal((n, 512)).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32))
+    rope = _bits((rng.standard_normal((n, 64)).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32))
+    slots = 64
+    lat_buf = np.zeros((slots, 512), np.uint8)
+    sc_buf = np.zeros(slots, np.float32)
+    rope_buf = np.zeros((slots, 64), np.uint16)
+    assert oracle.kv_quant_pth(lat, rope, [5, 6, 7], lat_buf, sc_buf, rope_buf) == 3
+    for r in range(n):
+        K = oracle.dequant_row_pth(lat_buf[5 + r], sc_buf[5 + r], rope_buf[5 + r])
+        x = (lat[r].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        y = (rope[r].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        s = float(sc_buf[5 + r])
+        assert np.all(np.abs(K[:512] - x) <= np.maximum(np.abs(x) / 16, 2.0 ** -10 * s) * (1 + 1e-6))
+        assert np.all(np.abs(K[512:] - y) <= np.abs(y) * 2.0 ** -8 * (1 + 1e-6))
+    # one selected row: the output is that row's latent exactly and lse is its score; the row twice: same
+    # output, lse + ln 2
+    q = _bits((rng.standard_normal((1, 1, 16, 576)).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32))
+    bt = np.array([[0]], np.int32)
+    K = oracle.dequant_row_pth(lat_buf[6], sc_buf[6], rope_buf[6])
+    qv = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[0, 0]
+    for idx, extra in (([6, -1], 0.0), ([6, 6], math.log(2.0))):
+        out, lse, _ = oracle.sparse_decode_pth(q, lat_buf, sc_buf, rope_buf, bt, [64], np.array([[idx]], np.int32), 0.1)
+        assert np.allclose(out[0, 0], np.broadcast_to(K[:512], (16, 512)), rtol=1e-14, atol=0)
+        assert np.allclose(lse[0, 0], 0.1 * (qv @ K) + extra, rtol=1e-12, atol=1e-12)
