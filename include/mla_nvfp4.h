@@ -184,6 +184,43 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
                         void* stream);
 
 /*
+ * TokenSpeed's per-token-head FP8 layout (TokenSpeed write-up, MLA KV layout section), a format variant for
+ * comparison: three slot-indexed buffers, the latent as E4M3 codes lat[slot*512 ..], one fp32 scale
+ * scale[slot], the rope part as bf16 rope[slot*64 ..].  Written per token, in fp32:
+ *     s = max(max_i |latent_i|, 1e-26) / 448,  lat_i = E4M3(latent_i / s) (nearest, ties to even),
+ *     rope_i = bf16(rope_in_i / s) (nearest, ties to even; inf past the bf16 range).
+ *   k_nope, k_rope    (device) bf16, k_nope 16-byte aligned with nope_stride a multiple of 8 (>= 512),
+ *                     rope_stride >= 64 elements
+ *   slot_mapping      (device) int64 [n]; slots < 0 or >= num_slots are skipped
+ *   lat               (device) [num_slots, 512] bytes, 8-byte aligned; scale (device) fp32 [num_slots];
+ *   rope              (device) bf16 [num_slots, 64]
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+int mla_kv_quant_pth(const void* k_nope, int64_t nope_stride, const void* k_rope, int64_t rope_stride,
+                     const int64_t* slot_mapping, int64_t n, void* lat, float* scale, void* rope, int64_t num_slots,
+                     void* stream);
+
+/*
+ * Sparse MLA decode over the per-token-head layout: the definition of mla_sparse_decode with position p of
+ * request b at slot = block_table[b*bt_stride + p/64]*64 + p%64 (page entries in [0, num_slots/64)), and
+ * K = (lat * scale, rope * scale), V = lat * scale (the inverse of the write).  Scores use FP16 latent
+ * operands (q rounded to fp16, the codes exact) and bf16 rope operands (exact), accumulated in fp32.
+ *   lat, scale, rope, num_slots    as written by mla_kv_quant_pth (lat and rope 16-byte aligned)
+ *   q, block_table, bt_stride, context_lens, indices, B, T, topk, sm_scale, causal, out, lse
+ *                  as for mla_sparse_decode; H in {16, 32, 64, 128}
+ *   num_splits     0 = the library's choice, else 1..64 (at most one split per 64 list entries)
+ *   workspace      >= mla_sparse_decode_pth_workspace_bytes(...) bytes, 256-byte aligned (the splits' fp32
+ *                  partial results; no zero-fill needed); may be NULL when that size is 0
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_STRIDE_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ */
+size_t mla_sparse_decode_pth_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
+int mla_sparse_decode_pth(const void* q, const void* lat, const float* scale, const void* rope, int64_t num_slots,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                          const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                          int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Sparse-indexer keys (analysis page, section "Four bits per latent value: where 352 comes from": 128 FP8
  * values plus a scale per token, stored the way DeepSeek's indexer is; the pages give no quantization
  * rule, and this one is the TokenSpeed write-up's per-token FP8 rule from its MLA KV layout section):

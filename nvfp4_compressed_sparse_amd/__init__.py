@@ -23,7 +23,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_index_key_quant", "mla_index_logits",
+    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
+    "mla_sparse_decode_pth_workspace_bytes", "mla_sparse_decode_pth", "mla_index_key_quant", "mla_index_logits",
     "mla_index_topk_workspace_bytes", "mla_index_topk",
 ]
 
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
         "mla_stage_nvfp4_fp8": (ctypes.c_int, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, P, P, P, P]),
+        "mla_kv_quant_pth": (ctypes.c_int, [P, i64, P, i64, P, i64, P, P, P, i64, P]),
+        "mla_sparse_decode_pth_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "mla_sparse_decode_pth": (ctypes.c_int, [P, P, P, P, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P, P,
+                                                 P, sz, P]),
         "mla_index_key_quant": (ctypes.c_int, [P, i64, P, i64, P, i64, i64, P]),
         "mla_index_logits": (ctypes.c_int, [P, P, i32, P, i64, i64, P, i64, P, i32, i32, i32, i32, P, i64, P]),
         "mla_index_topk_workspace_bytes": (sz, [i64, i64]),
@@ -253,6 +258,66 @@ def mla_stage_nvfp4_fp8(pool, page_stride_bytes, num_pages, block_table, context
                                    staged_lens.data_ptr(), _stream(stream))
     _check("mla_stage_nvfp4_fp8", st)
     return staged, staged_block_table, staged_lens
+
+
+# --------------------------------------------------------------------------- per-token-head FP8 layout
+
+def mla_kv_quant_pth(k_nope, k_rope, slot_mapping, lat, scale, rope, stream=None):
+    """Write n tokens in TokenSpeed's per-token-head FP8 layout (see include/mla_nvfp4.h): lat uint8
+    [slots, 512], scale float32 [slots], rope bfloat16 [slots, 64]."""
+    import torch
+    _dev(k_nope, torch.bfloat16, "k_nope")
+    _dev(k_rope, torch.bfloat16, "k_rope")
+    _dev(slot_mapping, torch.int64, "slot_mapping")
+    _dev(lat, torch.uint8, "lat")
+    _dev(scale, torch.float32, "scale")
+    _dev(rope, torch.bfloat16, "rope")
+    n = slot_mapping.numel()
+    if k_nope.dim() != 2 or k_nope.shape != (n, LATENT_DIM) or k_nope.stride(1) != 1:
+        raise ValueError("k_nope must be [n, 512] with unit inner stride")
+    if k_rope.dim() != 2 or k_rope.shape != (n, ROPE_DIM) or k_rope.stride(1) != 1:
+        raise ValueError("k_rope must be [n, 64] with unit inner stride")
+    slots = scale.numel()
+    if (lat.shape != (slots, LATENT_DIM) or rope.shape != (slots, ROPE_DIM) or not lat.is_contiguous()
+            or not rope.is_contiguous() or not scale.is_contiguous() or not slot_mapping.is_contiguous()):
+        raise ValueError("lat [slots, 512], scale [slots] and rope [slots, 64] must be contiguous")
+    st = lib().mla_kv_quant_pth(k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+                                slot_mapping.data_ptr(), n, lat.data_ptr(), scale.data_ptr(), rope.data_ptr(), slots,
+                                _stream(stream))
+    _check("mla_kv_quant_pth", st)
+
+
+def mla_sparse_decode_pth(q, lat, scale, rope, block_table, context_lens, indices, sm_scale, causal=False,
+                          num_splits=0, out=None, lse=None, stream=None):
+    """Sparse decode over the per-token-head layout (see include/mla_nvfp4.h).  Returns (out, lse)."""
+    import torch
+    _dev(q, torch.bfloat16, "q")
+    for t, dt, name in ((lat, torch.uint8, "lat"), (scale, torch.float32, "scale"), (rope, torch.bfloat16, "rope"),
+                        (block_table, torch.int32, "block_table"), (context_lens, torch.int32, "context_lens"),
+                        (indices, torch.int32, "indices")):
+        _dev(t, dt, name)
+    if q.dim() != 4 or q.shape[3] != QK_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, T, H, 576] tensor")
+    B, T, H, _ = q.shape
+    if indices.dim() != 3 or indices.shape[:2] != (B, T) or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [B, T, topk] tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, pages] tensor")
+    topk = indices.shape[2]
+    ws_bytes = lib().mla_sparse_decode_pth_workspace_bytes(B, T, H, topk, int(num_splits))
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if out is None:
+        out = torch.empty((B, T, H, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    st = lib().mla_sparse_decode_pth(q.data_ptr(), lat.data_ptr(), scale.data_ptr(), rope.data_ptr(), scale.numel(),
+                                     block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
+                                     indices.data_ptr(), B, T, H, topk, float(sm_scale), int(bool(causal)),
+                                     int(num_splits), out.data_ptr(), lse.data_ptr(),
+                                     None if workspace is None else workspace.data_ptr(),
+                                     0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("mla_sparse_decode_pth", st)
+    return out, lse
 
 
 # --------------------------------------------------------------------------- sparse-indexer keys and logits

@@ -251,3 +251,37 @@ def test_index_logits_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert call() == 5
+
+
+def test_pth_argument_errors():
+    def quant(**kw):
+        a = dict(kn=FAKE, ns=512, kr=FAKE, rs=64, sm=FAKE, n=8, lat=FAKE, sc=FAKE, rope=FAKE, slots=128)
+        a.update(kw)
+        return M.lib().mla_kv_quant_pth(a["kn"], a["ns"], a["kr"], a["rs"], a["sm"], a["n"], a["lat"], a["sc"],
+                                        a["rope"], a["slots"], None)
+    for name in ("kn", "kr", "sm", "lat", "sc", "rope"):
+        assert quant(**{name: None}) == 1, name
+    assert quant(n=-1) == 2 and quant(slots=0) == 2
+    assert quant(n=0, kn=None) == 0
+    assert quant(ns=511) == 3 and quant(ns=516) == 3 and quant(rs=63) == 3
+    assert quant(kn=FAKE + 8) == 3 and quant(lat=FAKE + 4) == 3
+
+    def dec(**kw):
+        a = dict(q=FAKE, lat=FAKE, sc=FAKE, rope=FAKE, slots=4096, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, B=2, T=1, H=32,
+                 k=256, scale=0.07, causal=0, S=0, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return M.lib().mla_sparse_decode_pth(a["q"], a["lat"], a["sc"], a["rope"], a["slots"], a["bt"], a["bts"],
+                                             a["ctx"], a["idx"], a["B"], a["T"], a["H"], a["k"], a["scale"],
+                                             a["causal"], a["S"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+    for name in ("q", "lat", "sc", "rope", "bt", "ctx", "idx", "out"):
+        assert dec(**{name: None}) == 1, name
+    assert dec(H=48) == 2 and dec(H=8) == 2 and dec(k=0) == 2 and dec(k=2049) == 2 and dec(S=65) == 2
+    assert dec(scale=0.0) == 2 and dec(scale=float("inf")) == 2 and dec(causal=3) == 2 and dec(slots=63) == 2
+    assert dec(S=8, k=256) == 2  # more splits than 64-entry chunks
+    assert dec(q=FAKE + 8) == 3 and dec(rope=FAKE + 8) == 3 and dec(out=FAKE + 2) == 3
+    need = M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 2)
+    assert need > 0 and M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 1) == 0
+    assert dec(S=2, wsb=need - 1) == 4 and dec(S=2, ws=None) == 1
+    import torch
+    if not torch.cuda.is_available():
+        assert quant() == 5 and dec(S=2, wsb=need) == 5
