@@ -104,9 +104,10 @@ def main():
     ap.add_argument("--pad-as-row0", action="store_true",
                     help="sparse workloads: replace the lists' -1 entries by position 0 before timing (the pages' "
                          "first version read row zero for each of them; a comparison, not the method's result)")
-    ap.add_argument("--path", default="native", choices=["native", "staged"],
-                    help="sparse workloads: native NVFP4 decode, or the staged path (unpack the selected rows "
-                         "to an FP8 copy, then the FP8 decoder reads it)")
+    ap.add_argument("--path", default="native", choices=["native", "staged", "pth"],
+                    help="sparse workloads: native NVFP4 decode, the staged path (unpack the selected rows "
+                         "to an FP8 copy, then the FP8 decoder reads it), or the per-token-head FP8 layout "
+                         "(FP8 latent, fp32 scale, bf16 rope in three buffers) and its decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -143,8 +144,9 @@ def main():
 
     cfg = W.CONFIGS[args.workload]
     staged_path = args.path == "staged"
-    if staged_path and not (cfg.topk and cfg.fmt == "nvfp4"):
-        raise SystemExit("--path staged applies to the sparse NVFP4 workloads")
+    pth_path = args.path == "pth"
+    if (staged_path or pth_path) and not (cfg.topk and cfg.fmt == "nvfp4"):
+        raise SystemExit("--path staged / pth apply to the sparse NVFP4 workloads")
     dev = "cuda"
     torch.cuda.set_device(0)
     log(f"[bench] workload {cfg.name}: B={cfg.B} T={cfg.T} H={cfg.H} topk={cfg.topk} fmt={cfg.fmt}")
@@ -165,9 +167,17 @@ def main():
                                                 for b in range(cfg.B)]).astype(np.int64)).to(dev)
         w_lat, w_rope, w_slots = inp["lat"][rows].contiguous(), inp["rope"][rows].contiguous(), inp["slots"][rows]
 
+    if pth_path:  # the same rows in the per-token-head layout
+        pth_slots = lay.num_pages * 64
+        pth_lat = torch.zeros((pth_slots, 512), dtype=torch.uint8, device=dev)
+        pth_sc = torch.zeros(pth_slots, dtype=torch.float32, device=dev)
+        pth_rope = torch.zeros((pth_slots, 64), dtype=torch.bfloat16, device=dev)
+        M.mla_kv_quant_pth(inp["lat"], inp["rope"], inp["slots"], pth_lat, pth_sc, pth_rope)
+        torch.cuda.synchronize()
+
     # oracle sample (built before the source rows are released)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not pth_path:  # the oracle sample covers the NVFP4 rows
         cpu = prepare_cpu_sample(cfg, inp, args.cpu_sample)
     del inp["lat"], inp["rope"], inp["slots"]
     torch.cuda.empty_cache()
@@ -209,8 +219,21 @@ def main():
         valid = [int(sum(min(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1, int(lay.ctx[b]))
                          for b in range(cfg.B) for t in range(cfg.T)))] * N_SETS
 
+    if pth_path:
+        S = args.splits or 0
+        pth_ws = M.lib().mla_sparse_decode_pth_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S)
+
     def step(i, ev=None):
         k = i % N_SETS
+        if pth_path:
+            M.mla_kv_quant_pth(w_lat, w_rope, w_slots, pth_lat, pth_sc, pth_rope, stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+            M.mla_sparse_decode_pth(q_sets[k], pth_lat, pth_sc, pth_rope, inp["bt"], inp["ctx"], idx_sets[k],
+                                    cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         quant(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
         if ev is not None:
             ev[0].record(stream)
@@ -262,6 +285,8 @@ def main():
     if staged_path:
         # the staged path moves a selected row three times: 352 B read, 576 B FP8 copy written and read
         bytes_per += int(vrows * 2 * 576)
+    if pth_path:  # a per-token-head row is 512 + 4 + 128 bytes
+        bytes_per += int(vrows * (644 - cfg.row_bytes))
     if cfg.H <= 32:
         ach = bytes_per / (dec_avg_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -270,13 +295,16 @@ def main():
         ach = flops_per / (dec_avg_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-    t = None if staged_path else profile_record(cfg, "traffic", "traffic_bytes_per_launch")
+    t = None if (staged_path or pth_path) else profile_record(cfg, "traffic", "traffic_bytes_per_launch")
     roof["traffic"] = None if t is None else int(t)
     if cfg.H > 32:
         roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent")
     if staged_path:
         roof["kernel"] = ("mla_stage_nvfp4_fp8 + mla_dense_decode_fp8 calls: stage_rows_kernel then decode_kernel "
                           "over the FP8 copy, timed together with HIP events on their stream")
+    elif pth_path:
+        roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), timed "
+                          "with HIP events on their stream")
     else:
         roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + " call: " + \
             ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
@@ -301,6 +329,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "q_len": cfg.T, "H": cfg.H, "topk": cfg.topk,
                    "context": cfg.ctx or list(cfg.ctx_range), "row_bytes": cfg.row_bytes, "page_tokens": 64,
                    "causal": cfg.causal, "splits": S, "path": args.path,
+                   "row_bytes_read": 644 if pth_path else cfg.row_bytes,
                    "index_padding": "position 0" if args.pad_as_row0 else "-1 (skipped)",
                    "step": ("quantize %d rows + %s" % (cfg.quant_chunk or nq,
                                                        "stage + FP8 decode" if staged_path else "decode"))},
