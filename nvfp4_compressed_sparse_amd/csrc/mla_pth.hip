@@ -6,17 +6,21 @@
 // pth_quant_kernel: one wave per token; lane l holds latent values 8l..8l+7 and rope value l.
 //
 // pth_decode_kernel: one 256-thread workgroup per (query token, group of 16 heads, split).  The split's
-// list entries are resolved to slots (order kept) in LDS; then, per step of 64 rows, wave w scores rows
-// 16w..16w+15 of the step for the 16 heads with MFMA 16x16x32: the latent part in f16 (q rounded to f16,
-// the codes exact), the rope part in bf16 (both exact), one accumulator.  Lane l holds, for row l%16, the
-// latent bytes 128(l/16)..+127 and rope dims 16(l/16)..+15, and in latent k-step ks feeds bytes 8ks..+7
-// of them (q's fragments use the same dimension order).  The row's scale multiplies the scores; each
-// wave keeps its own online softmax (heads 4(l/16)+i of the accumulator lane), folds the row scale into
-// P, and accumulates O += P V with MFMA 16x16x16 f16: P goes through LDS to the A layout (head l%16, rows
-// 4(l/16)..+3); V is the wave's rows staged in LDS, lane (c, g) reading rows 4g..4g+3 at columns
-// 64cq+4c..+3 and transposing the 4x4 bytes with byte permutes, so that its tile 4cq+e covers column
-// 64cq+4c+e.  The four waves' states merge elementwise through LDS; with several splits the normalized
-// result and its log-sum-exp go to the workspace and pth_merge_kernel combines them.
+// list entries are resolved to slots (order kept) in LDS; then, per step of 64 rows:
+//   * wave w scores rows 16w..16w+15 of the step for the 16 heads with MFMA 16x16x32: the latent part in
+//     f16 (q rounded to f16, the codes exact), the rope part in bf16 (both exact), one accumulator.  Lane
+//     l holds, for row l%16, the latent bytes 128(l/16)..+127 and rope dims 16(l/16)..+15, and in latent
+//     k-step ks feeds bytes 8ks..+7 of them (q's fragments use the same dimension order).  The scores
+//     (times the row's scale), the scales and the latent rows go to LDS; the next step's rows are already
+//     loading into a second register buffer;
+//   * 16 threads per head take the step's softmax: the running max, P' = p * row scale (V's scale folded
+//     into P) as f16 in LDS, the running sum, the rescale factor;
+//   * wave w accumulates O += P' V for its 128 output columns over the step's 64 rows with MFMA
+//     16x16x16 f16: lane (c, g) reads rows 4g..4g+3 of a 16-row k-step at columns 64cq+4c..+3 from the
+//     staged rows and transposes the 4x4 bytes with byte permutes, so that its tile 4cq+e covers column
+//     64cq+4c+e.
+// Each wave writes its own columns at the end; with several splits the normalized result and its
+// log-sum-exp go to the workspace and pth_merge_kernel combines them.
 #include "mla_device.h"
 #include "mla_pth_internal.h"
 
@@ -64,10 +68,12 @@ __global__ __launch_bounds__(256) void pth_quant_kernel(PthQuantArgs a) {
 struct PthShared {
   uint32_t slots[kPthMaxChunk];
   int wcount[4];
-  uint8_t stage[4][16][528];      // a wave's 16 latent rows (512 bytes + 16 padding)
-  _Float16 pt[4][16][24];         // a wave's P^T: head, row (16 + 8 padding)
-  float mo[2][128][64];           // merge: O values, [value][lane]
-  float ml[2][8][64];             // merge: m[4], l[4] per lane
+  uint8_t stage[2][64][528];      // the step's 64 latent rows (512 bytes + 16 padding), two steps
+  float sz[64][17];               // the step's scores z[row][head] (log2 units), row 16w + lane%16 by wave w
+  float ss[64];                   // the step's row scales
+  _Float16 pp[16][72];            // P'[head][row] = p * row scale (f16), rows padded by 8
+  float salpha[16];               // the step's rescale factor per head
+  float sl[16], sm[16];           // the final l and m per head
 };
 
 // 4 E4M3 bytes -> f16x4 (exact)
@@ -81,9 +87,12 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int S = a.splits, HG = a.H / 16;
-  const int s_idx = blockIdx.x % S;
-  const int hg = (blockIdx.x / S) % HG;
-  const int64_t id = blockIdx.x / (S * HG);
+  // the head groups of one (token, split) read the same rows: they take consecutive logical ids, which
+  // run on one XCD and so share its L2
+  const int j = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int hg = j % HG;
+  const int s_idx = (j / HG) % S;
+  const int64_t id = j / (HG * S);
   const int b = (int)(id / a.T), t = (int)(id % a.T);
   const int L = a.ctx[b];
   const int lim = a.causal ? L - a.T + t : L - 1;
@@ -93,14 +102,30 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
   const int e0 = s_idx * a.chunk;
   uint32_t slot_k[kPthEPT];
   uint32_t vmask = 0;
+  // every load is issued (an entry past the list reads entry 0, a position outside the table reads
+  // page-table entry 0) and its result discarded afterwards: the loads of all entries fly together
+  int pos_k[kPthEPT];
 #pragma unroll
   for (int k = 0; k < kPthEPT; ++k) {
     const int e = e0 + kPthEPT * tid + k;
-    const int pos = (kPthEPT * tid + k < a.chunk && e < a.topk) ? a.indices[id * a.topk + e] : -1;
+    const bool in_list = kPthEPT * tid + k < a.chunk && e < a.topk;
+    const int v = a.indices[id * a.topk + (in_list ? e : 0)];
+    pos_k[k] = in_list ? v : -1;
+  }
+  int32_t page_k[kPthEPT];
+#pragma unroll
+  for (int k = 0; k < kPthEPT; ++k) {
+    const int pos = pos_k[k];
     const int pg = (pos >= 0 ? pos : 0) >> 6;
     const bool inr = pos >= 0 && pos <= lim && pg < a.bt_stride;
-    const int64_t page = inr ? a.block_table[(int64_t)b * a.bt_stride + pg] : -1;
-    const bool ok = inr && page >= 0 && page < num_pages;
+    page_k[k] = a.block_table[(int64_t)b * a.bt_stride + (inr ? pg : 0)];
+    pos_k[k] = inr ? pos : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < kPthEPT; ++k) {
+    const int pos = pos_k[k];
+    const int64_t page = page_k[k];
+    const bool ok = pos >= 0 && page >= 0 && page < num_pages;
     slot_k[k] = ok ? (uint32_t)(page * 64 + (pos & 63)) : 0u;
     vmask |= (uint32_t)ok << k;
   }
@@ -143,161 +168,169 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
   for (int j = 0; j < 2; ++j)
     qr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 512 + 16 * g + 8 * j));
 
-  // ---- the wave's online softmax over its rows: heads 4g + i of this lane group
-  float m[4], l[4];
+  // softmax role: thread tid serves head sh_h = tid / 16 over rows 4 * (tid % 16) .. +3 of a step
+  const int sh_h = tid >> 4, sh_r = 4 * (tid & 15);
+  float m_h = -INFINITY, l_h = 0.0f;
+  // accumulate role: wave w owns columns 128w .. 128w + 127 as column quads cq = 2w, 2w + 1; tile
+  // 4c + e (c < 2) covers column 64(2w + c) + 4(lane%16) + e, heads 4g + i
+  f32x4 o[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-  }
-  f32x4 o[32];  // tile 4cq + e: column 64cq + 4(l%16) + e, heads 4g + i
-#pragma unroll
-  for (int j = 0; j < 32; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nsteps = (n + 63) / 64;
-  for (int st = 0; st < nsteps; ++st) {
-    const int row = st * 64 + 16 * w + r16;
-    const bool valid = row < n;
-    const uint32_t slot = sh.slots[valid ? row : 0];
-    const uint8_t* lp = a.lat + (uint64_t)slot * 512 + 128 * g;
+  // a step's rows for this lane: latent bytes 128g..+127, rope dims 16g..+15 and the scale of row
+  // 16w + r16 of the step
+  struct StepRows {
     u32x4 kl[8];
+    u32x4 kr[2];
+    float sc;
+    bool valid;
+  };
+  auto load_step = [&](int st, StepRows& sr) {
+    const int row = st * 64 + 16 * w + r16;
+    sr.valid = row < n;
+    const uint32_t listed = sh.slots[sr.valid ? row : 0];  // slots[0] may be unset when n = 0
+    const uint32_t slot = sr.valid ? listed : 0u;
+    const uint8_t* lp = a.lat + (uint64_t)slot * 512 + 128 * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kl[j] = *reinterpret_cast<const u32x4*>(lp + 16 * j);
+    for (int j = 0; j < 8; ++j) sr.kl[j] = *reinterpret_cast<const u32x4*>(lp + 16 * j);
     const uint16_t* rp = a.rope + (uint64_t)slot * 64 + 16 * g;
-    const u32x4 kr0 = *reinterpret_cast<const u32x4*>(rp);
-    const u32x4 kr1 = *reinterpret_cast<const u32x4*>(rp + 8);
-    const float sc = a.scale[slot];
-
-    // scores: C[head 4g + i][row r16]
+    sr.kr[0] = *reinterpret_cast<const u32x4*>(rp);
+    sr.kr[1] = *reinterpret_cast<const u32x4*>(rp + 8);
+    sr.sc = a.scale[slot];
+  };
+  auto compute_step = [&](int st, const StepRows& sr) {
+    const int buf = st & 1;
+    // ---- scores of the wave's 16 rows: C[head 4g + i][row r16]; stage the rows for P V
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      const uint32_t d0 = kl[ks >> 1][(ks & 1) * 2], d1 = kl[ks >> 1][(ks & 1) * 2 + 1];
+      const uint32_t d0 = sr.kl[ks >> 1][(ks & 1) * 2], d1 = sr.kl[ks >> 1][(ks & 1) * 2 + 1];
       const f16x8 kb = as_f16x8(e4m3x2_to_f16<false>(d0), e4m3x2_to_f16<true>(d0), e4m3x2_to_f16<false>(d1),
                                 e4m3x2_to_f16<true>(d1));
       acc = mfma16x16x32(qa[ks], kb, acc);
     }
-    acc = mfma16x16x32(qr[0], __builtin_bit_cast(bf16x8, kr0), acc);
-    acc = mfma16x16x32(qr[1], __builtin_bit_cast(bf16x8, kr1), acc);
+    acc = mfma16x16x32(qr[0], __builtin_bit_cast(bf16x8, sr.kr[0]), acc);
+    acc = mfma16x16x32(qr[1], __builtin_bit_cast(bf16x8, sr.kr[1]), acc);
+    const int row = 16 * w + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.sz[row][4 * g + i] = sr.valid ? acc[i] * sr.sc * a.scale_log2 : -INFINITY;
+    // a row past the list stages zeros with scale 0, so that whatever slot 0 holds (it is read in its
+    // place) cannot reach O through 0 * NaN
+    if (g == 0) sh.ss[row] = sr.valid ? sr.sc : 0.0f;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sh.stage[buf][row][128 * g + 16 * j]) = sr.valid ? sr.kl[j] : zero4;
+    lds_barrier();  // (A) scores, scales and rows of the step complete; the next rows stay in flight
 
-    // stage the latent rows for P V (the wave's own region; no other wave reads it)
+    // ---- softmax over the step's 64 rows, head sh_h: the running max, P' = p * row scale, the sum
+    float z[4], mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sh.stage[w][r16][128 * g + 16 * j]) = kl[j];
-
-    float p[4], alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float z = valid ? acc[i] * sc * a.scale_log2 : -INFINITY;
-      float mx = z;
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 16));
-      const float mn = fmaxf(m[i], mx);
-      const bool live = mn != -INFINITY;  // some row of this head seen so far
-      alpha[i] = live ? exp2f(m[i] - mn) : 1.0f;
-      p[i] = live ? exp2f(z - mn) : 0.0f;
-      float ps = p[i];
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) ps += __shfl_xor(ps, d, 16);
-      l[i] = l[i] * alpha[i] + ps;
-      m[i] = mn;
-      sh.pt[w][4 * g + i][r16] = (_Float16)(p[i] * sc);  // V's row scale folded into P
+    for (int r = 0; r < 4; ++r) {
+      z[r] = sh.sz[sh_r + r][sh_h];
+      mx = fmaxf(mx, z[r]);
     }
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
+    for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 16));
+    const float mn = fmaxf(m_h, mx);
+    const bool live = mn != -INFINITY;  // some row of this head seen so far
+    const float alpha = live ? exp2f(m_h - mn) : 1.0f;
+    float ps = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-    // the stage and P^T writes of this wave are visible to its own later reads after lgkmcnt(0)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
-
-    // P^T as the A operand: head l%16, rows 4g..4g+3
-    const f16x4 pa = *reinterpret_cast<const f16x4*>(&sh.pt[w][r16][4 * g]);
-#pragma unroll
-    for (int cq = 0; cq < 8; ++cq) {
-      uint32_t d[4];  // rows 4g + i, columns 64cq + 4r16 .. +3
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const uint32_t*>(&sh.stage[w][4 * g + i][64 * cq + 4 * r16]);
-      const uint32_t p01a = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);  // d0[0] d1[0] d0[1] d1[1]
-      const uint32_t p23a = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
-      const uint32_t p01b = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);  // d0[2] d1[2] d0[3] d1[3]
-      const uint32_t p23b = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
-      const uint32_t col[4] = {__builtin_amdgcn_perm(p23a, p01a, 0x05040100u),
-                               __builtin_amdgcn_perm(p23a, p01a, 0x07060302u),
-                               __builtin_amdgcn_perm(p23b, p01b, 0x05040100u),
-                               __builtin_amdgcn_perm(p23b, p01b, 0x07060302u)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[4 * cq + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, e4m3x4_to_f16x4(col[e]), o[4 * cq + e], 0, 0, 0);
+    for (int r = 0; r < 4; ++r) {
+      const float p = live ? exp2f(z[r] - mn) : 0.0f;
+      ps += p;
+      sh.pp[sh_h][sh_r + r] = (_Float16)(p * sh.ss[sh_r + r]);  // V's row scale folded into P
     }
-    __builtin_amdgcn_wave_barrier();  // the next step's stage writes follow this step's reads
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) ps += __shfl_xor(ps, d, 16);
+    l_h = l_h * alpha + ps;
+    m_h = mn;
+    if ((tid & 15) == 0) sh.salpha[sh_h] = alpha;
+    lds_barrier();  // (B) P' and the rescale factors complete
+
+    // ---- O[heads][the wave's columns] = alpha O + P' V over the step's 64 rows (4 k-steps of 16)
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = sh.salpha[4 * g + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[j][i] *= al[i];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const f16x4 pa = *reinterpret_cast<const f16x4*>(&sh.pp[r16][16 * kk + 4 * g]);  // head lane%16
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int cq = 2 * w + c;
+        uint32_t d[4];  // rows 16kk + 4g + i, columns 64cq + 4r16 .. +3
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d[i] = *reinterpret_cast<const uint32_t*>(&sh.stage[buf][16 * kk + 4 * g + i][64 * cq + 4 * r16]);
+        const uint32_t p01a = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);  // d0[0] d1[0] d0[1] d1[1]
+        const uint32_t p23a = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+        const uint32_t p01b = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);  // d0[2] d1[2] d0[3] d1[3]
+        const uint32_t p23b = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+        const uint32_t col[4] = {__builtin_amdgcn_perm(p23a, p01a, 0x05040100u),
+                                 __builtin_amdgcn_perm(p23a, p01a, 0x07060302u),
+                                 __builtin_amdgcn_perm(p23b, p01b, 0x05040100u),
+                                 __builtin_amdgcn_perm(p23b, p01b, 0x07060302u)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[4 * c + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, e4m3x4_to_f16x4(col[e]), o[4 * c + e], 0, 0, 0);
+      }
+    }
+  };
+  // two register buffers named statically (a copy between them would wait for loads in flight): step
+  // st + 1's rows load while step st computes.  The loads are unconditional (a step past the end reads
+  // slot 0 and is never used) so that the compiler's counter waits stay exact.  The stage alternates
+  // between two buffers, so the next step's rows never overwrite rows still being read; barriers (A)
+  // and (B) order the rest.
+  const int nsteps = (n + 63) / 64;
+  StepRows ra, rb;
+  load_step(0, ra);
+  // The scheduling barriers keep the compiler from hoisting a step's first conversions above the next
+  // step's loads, which would make them wait for the loads just issued.
+  for (int st = 0; st < nsteps; st += 2) {
+    load_step(st + 1, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(st, ra);
+    if (st + 1 >= nsteps) break;
+    load_step(st + 2, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(st + 1, rb);
   }
 
-  // ---- merge the four waves' states: 2,3 into 0,1, then 1 into 0
-  auto merge_from = [&](int buf) {
-    float mb[4], lb[4], f_self[4], f_other[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mb[i] = sh.ml[buf][i][lane];
-      lb[i] = sh.ml[buf][4 + i][lane];
-      const float mn = fmaxf(m[i], mb[i]);
-      f_self[i] = mn == -INFINITY ? 0.0f : exp2f(m[i] - mn);
-      f_other[i] = mn == -INFINITY ? 0.0f : exp2f(mb[i] - mn);
-      l[i] = l[i] * f_self[i] + lb[i] * f_other[i];
-      m[i] = mn;
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[j][i] = o[j][i] * f_self[i] + sh.mo[buf][4 * j + i][lane] * f_other[i];
-  };
-  auto store_to = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sh.ml[buf][i][lane] = m[i];
-      sh.ml[buf][4 + i][lane] = l[i];
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh.mo[buf][4 * j + i][lane] = o[j][i];
-  };
-  if (w >= 2) store_to(w - 2);
+  // ---- the normalized result of the wave's columns and the log-sum-exp
+  if ((tid & 15) == 0) {
+    sh.sl[sh_h] = l_h;
+    sh.sm[sh_h] = m_h;
+  }
   __syncthreads();
-  if (w < 2) merge_from(w);
-  __syncthreads();
-  if (w == 1) store_to(0);
-  __syncthreads();
-  if (w != 0) return;
-  merge_from(0);
-
-  // ---- wave 0: normalized result (heads 4g + i, columns 64cq + 4r16 + e) and its log-sum-exp
   float inv[4], lse[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    inv[i] = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
-    lse[i] = l[i] > 0.0f ? (m[i] + __log2f(l[i])) * 0.6931471805599453f : -INFINITY;
+    const float lv = sh.sl[4 * g + i], mv = sh.sm[4 * g + i];
+    inv[i] = lv > 0.0f ? 1.0f / lv : 0.0f;
+    lse[i] = lv > 0.0f ? (mv + __log2f(lv)) * 0.6931471805599453f : -INFINITY;
   }
   const int64_t hrow0 = id * a.H + 16 * hg + 4 * g;
-  if (S == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t* dst = a.out + (hrow0 + i) * 512 + 4 * r16;
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int cq = 0; cq < 8; ++cq)
-        *reinterpret_cast<u32x2*>(dst + 64 * cq) =
-            u32x2{pack_bf16_rne(o[4 * cq][i] * inv[i], o[4 * cq + 1][i] * inv[i]),
-                  pack_bf16_rne(o[4 * cq + 2][i] * inv[i], o[4 * cq + 3][i] * inv[i])};
-      if (a.lse && r16 == 0) a.lse[hrow0 + i] = lse[i];
+    for (int c = 0; c < 2; ++c) {
+      const int col0 = 64 * (2 * w + c) + 4 * r16;
+      const f32x4 v = {o[4 * c][i] * inv[i], o[4 * c + 1][i] * inv[i], o[4 * c + 2][i] * inv[i], o[4 * c + 3][i] * inv[i]};
+      if (S == 1)
+        *reinterpret_cast<u32x2*>(a.out + (hrow0 + i) * 512 + col0) = u32x2{pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3])};
+      else
+        *reinterpret_cast<f32x4*>(a.part_o + ((hrow0 + i) * S + s_idx) * 512 + col0) = v;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* dst = a.part_o + ((hrow0 + i) * S + s_idx) * 512 + 4 * r16;
-#pragma unroll
-      for (int cq = 0; cq < 8; ++cq)
-        *reinterpret_cast<f32x4*>(dst + 64 * cq) =
-            f32x4{o[4 * cq][i] * inv[i], o[4 * cq + 1][i] * inv[i], o[4 * cq + 2][i] * inv[i], o[4 * cq + 3][i] * inv[i]};
-      if (r16 == 0) a.part_lse[(hrow0 + i) * S + s_idx] = lse[i];
+    if (w == 0 && r16 == 0) {
+      if (S == 1) {
+        if (a.lse) a.lse[hrow0 + i] = lse[i];
+      } else {
+        a.part_lse[(hrow0 + i) * S + s_idx] = lse[i];
+      }
     }
   }
 }
