@@ -506,7 +506,10 @@ def bench_index_logits(args):
     ach = bytes_per / (call_avg * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "mla_index_logits call: index_logits_kernel<%d>, timed with HIP events on its stream" % HI,
+            # q and w of a request's tokens go to LDS when they fit 72 KB (272 + 4 bytes per token and
+            # head), else q stays in registers
+            "kernel": "mla_index_logits call: %s<%d>, timed with HIP events on its stream"
+                      % ("index_logits_multi_kernel" if cfg.T * HI * 276 <= 72 * 1024 else "index_logits_kernel", HI),
             "algorithmic_bytes_per_launch": bytes_per, "flops_per_launch": flops,
             "mfma_tflops": round(flops / (call_avg * 1e-6) / 1e12, 1), "launch_us": round(call_avg, 3)}
     res = {

@@ -88,11 +88,16 @@ __global__ __launch_bounds__(256) void index_logits_kernel(IndexLogitsArgs a) {
   if (pg_first * 64 >= p_end) return;
   const int n_pages = min(kIdxPagesPerWave, (p_end - pg_first * 64 + 63) / 64);
 
-  // a page's keys, or page 0 of the pool (always readable; its values are discarded) for a page whose
-  // table entry is outside the pool or past the wave's pages: the loads stay unconditional, so the
-  // compiler can keep two pages in flight with exact waits
-  auto page_base = [&](int pg, bool& ok) -> const uint8_t* {
-    const int64_t phys = pg < a.bt_stride ? a.block_table[(int64_t)b * a.bt_stride + pg] : -1;
+  // the wave's page-table entries, loaded once (lane j: page pg_first + j; entry 0 read in place of an
+  // entry past the table) so that no page waits for its own table lookup
+  const int pj = pg_first + (lane < kIdxPagesPerWave ? lane : 0);
+  const int32_t tab = a.block_table[(int64_t)b * a.bt_stride + (pj < a.bt_stride ? pj : 0)];
+  const int32_t phys_lane = pj < a.bt_stride ? tab : -1;
+  // the keys of the wave's page i, or page 0 of the pool (always readable; its values are discarded)
+  // for a page whose table entry is outside the pool or past the wave's pages: the loads stay
+  // unconditional, so the compiler can keep pages in flight with exact waits
+  auto page_base = [&](int i, bool& ok) -> const uint8_t* {
+    const int64_t phys = __builtin_amdgcn_readlane(phys_lane, i);
     ok = phys >= 0 && phys < a.num_pages;
     return a.pool + (ok ? phys : 0) * a.page_stride;
   };
@@ -119,13 +124,13 @@ __global__ __launch_bounds__(256) void index_logits_kernel(IndexLogitsArgs a) {
     // which would wait for loads still in flight)
     IndexPage buf[3];
     bool ok[3];
-    load_index_page(page_base(pg_first, ok[0]), r16, g, lane, buf[0]);
-    load_index_page(page_base(pg_first + (n_pages > 1 ? 1 : 0), ok[1]), r16, g, lane, buf[1]);
+    load_index_page(page_base(0, ok[0]), r16, g, lane, buf[0]);
+    load_index_page(page_base(n_pages > 1 ? 1 : 0, ok[1]), r16, g, lane, buf[1]);
 #pragma unroll
     for (int i = 0; i < kIdxPagesPerWave; ++i) {
       if (i >= n_pages) break;
       if (i + 2 < kIdxPagesPerWave)
-        load_index_page(page_base(pg_first + (i + 2 < n_pages ? i + 2 : i), ok[(i + 2) % 3]), r16, g, lane,
+        load_index_page(page_base(i + 2 < n_pages ? i + 2 : i, ok[(i + 2) % 3]), r16, g, lane,
                         buf[(i + 2) % 3]);
       const IndexPage& cur = buf[i % 3];
       float tot[4];
@@ -190,20 +195,24 @@ __global__ __launch_bounds__(256) void index_logits_multi_kernel(IndexLogitsArgs
   const int p_end = L < a.ld ? L : (int)a.ld;
   if (pg_first * 64 >= p_end) return;
   const int n_pages = min(kIdxPagesPerWave, (p_end - pg_first * 64 + 63) / 64);
-  auto page_base = [&](int pg, bool& ok) -> const uint8_t* {
-    const int64_t phys = pg < a.bt_stride ? a.block_table[(int64_t)b * a.bt_stride + pg] : -1;
+  // the wave's page-table entries, loaded once (lane j: page pg_first + j), as in index_logits_kernel
+  const int pj = pg_first + (lane < kIdxPagesPerWave ? lane : 0);
+  const int32_t tab = a.block_table[(int64_t)b * a.bt_stride + (pj < a.bt_stride ? pj : 0)];
+  const int32_t phys_lane = pj < a.bt_stride ? tab : -1;
+  auto page_base = [&](int i, bool& ok) -> const uint8_t* {
+    const int64_t phys = __builtin_amdgcn_readlane(phys_lane, i);
     ok = phys >= 0 && phys < a.num_pages;
     return a.pool + (ok ? phys : 0) * a.page_stride;
   };
 
   IndexPage buf[2];
   bool ok[2];
-  load_index_page(page_base(pg_first, ok[0]), r16, g, lane, buf[0]);
+  load_index_page(page_base(0, ok[0]), r16, g, lane, buf[0]);
 #pragma unroll
   for (int i = 0; i < kIdxPagesPerWave; ++i) {
     if (i >= n_pages) break;
     if (i + 1 < kIdxPagesPerWave)
-      load_index_page(page_base(pg_first + (i + 1 < n_pages ? i + 1 : i), ok[(i + 1) % 2]), r16, g, lane,
+      load_index_page(page_base(i + 1 < n_pages ? i + 1 : i, ok[(i + 1) % 2]), r16, g, lane,
                       buf[(i + 1) % 2]);
     const IndexPage& cur = buf[i % 2];
     bf16x8 kf[4][4];  // tile nt, k-step ks: key bytes 8ks..8ks+7 of the lane's 32
