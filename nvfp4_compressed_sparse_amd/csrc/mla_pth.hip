@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void pth_quant_kernel(PthQuantArgs a) {
 struct PthShared {
   uint32_t slots[kPthMaxChunk];
   int wcount[4];
-  uint8_t stage[2][64][528];      // the step's 64 latent rows (512 bytes + 16 padding), two steps
+  uint8_t stage[64][528];         // the step's 64 latent rows (512 bytes + 16 padding)
+  _Float16 qs[16][520];           // the 16 heads' latent q as f16 (512 values + 8 padding)
   float sz[64][17];               // the step's scores z[row][head] (log2 units), row 16w + lane%16 by wave w
   float ss[64];                   // the step's row scales
   _Float16 pp[16][72];            // P'[head][row] = p * row scale (f16), rows padded by 8
@@ -82,7 +83,7 @@ __device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t w) {
   return f16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-__global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a) {
+__global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArgs a) {
   __shared__ __attribute__((aligned(16))) PthShared sh;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -147,22 +148,25 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
 #pragma unroll
   for (int k = 0; k < kPthEPT; ++k)
     if (vmask & (1u << k)) sh.slots[off++] = slot_k[k];
+  {  // the 16 heads' latent q to LDS as f16: thread tid takes head tid / 16, dims 32 (tid % 16) .. +31
+    const uint16_t* qsrc = a.q + (id * a.H + 16 * hg + (tid >> 4)) * 576 + 32 * (tid & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qsrc + 8 * j);
+      f16x8 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = (_Float16)bf16_to_f32(v[i] & 0xFFFFu);
+        f[2 * i + 1] = (_Float16)bf16_to_f32(v[i] >> 16);
+      }
+      *reinterpret_cast<f16x8*>(&sh.qs[tid >> 4][32 * (tid & 15) + 8 * j]) = f;
+    }
+  }
   __syncthreads();
 
-  // ---- q fragments of head 16hg + r16: latent dims 128g + 8ks .. +7 as f16, rope dims 16g + 8kr .. +7
+  // ---- q fragments of head 16hg + r16: latent dims 128g + 8ks .. +7 from LDS in each step, rope dims
+  // 16g + 8kr .. +7 in registers
   const uint16_t* qh = a.q + (id * a.H + 16 * hg + r16) * 576;
-  f16x8 qa[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(qh + 128 * g + 8 * j);
-    f16x8 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = (_Float16)bf16_to_f32(v[i] & 0xFFFFu);
-      f[2 * i + 1] = (_Float16)bf16_to_f32(v[i] >> 16);
-    }
-    qa[j] = f;
-  }
   bf16x8 qr[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -198,29 +202,31 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
     sr.kr[1] = *reinterpret_cast<const u32x4*>(rp + 8);
     sr.sc = a.scale[slot];
   };
-  auto compute_step = [&](int st, const StepRows& sr) {
-    const int buf = st & 1;
-    // ---- scores of the wave's 16 rows: C[head 4g + i][row r16]; stage the rows for P V
+  auto compute_step = [&](const StepRows& sr) {
+    // ---- scores of the wave's 16 rows: C[head 4g + i][row r16]
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       const uint32_t d0 = sr.kl[ks >> 1][(ks & 1) * 2], d1 = sr.kl[ks >> 1][(ks & 1) * 2 + 1];
       const f16x8 kb = as_f16x8(e4m3x2_to_f16<false>(d0), e4m3x2_to_f16<true>(d0), e4m3x2_to_f16<false>(d1),
                                 e4m3x2_to_f16<true>(d1));
-      acc = mfma16x16x32(qa[ks], kb, acc);
+      acc = mfma16x16x32(*reinterpret_cast<const f16x8*>(&sh.qs[r16][128 * g + 8 * ks]), kb, acc);
     }
     acc = mfma16x16x32(qr[0], __builtin_bit_cast(bf16x8, sr.kr[0]), acc);
     acc = mfma16x16x32(qr[1], __builtin_bit_cast(bf16x8, sr.kr[1]), acc);
     const int row = 16 * w + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sh.sz[row][4 * g + i] = sr.valid ? acc[i] * sr.sc * a.scale_log2 : -INFINITY;
-    // a row past the list stages zeros with scale 0, so that whatever slot 0 holds (it is read in its
-    // place) cannot reach O through 0 * NaN
+    // a row past the list gets scale 0 and stages zeros, so that whatever slot 0 holds (it is read in
+    // its place) cannot reach O through 0 * NaN
     if (g == 0) sh.ss[row] = sr.valid ? sr.sc : 0.0f;
+    lds_barrier();  // (A) scores and scales complete, every wave done with the last step's rows; the
+                    // next rows stay in flight
+
+    // ---- stage the rows for P V (one buffer: the last step's readers have all passed (A))
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sh.stage[buf][row][128 * g + 16 * j]) = sr.valid ? sr.kl[j] : zero4;
-    lds_barrier();  // (A) scores, scales and rows of the step complete; the next rows stay in flight
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sh.stage[row][128 * g + 16 * j]) = sr.valid ? sr.kl[j] : zero4;
 
     // ---- softmax over the step's 64 rows, head sh_h: the running max, P' = p * row scale, the sum
     float z[4], mx = -INFINITY;
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
     l_h = l_h * alpha + ps;
     m_h = mn;
     if ((tid & 15) == 0) sh.salpha[sh_h] = alpha;
-    lds_barrier();  // (B) P' and the rescale factors complete
+    lds_barrier();  // (B) P', the rescale factors and the staged rows complete
 
     // ---- O[heads][the wave's columns] = alpha O + P' V over the step's 64 rows (4 k-steps of 16)
     float al[4];
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
         uint32_t d[4];  // rows 16kk + 4g + i, columns 64cq + 4r16 .. +3
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          d[i] = *reinterpret_cast<const uint32_t*>(&sh.stage[buf][16 * kk + 4 * g + i][64 * cq + 4 * r16]);
+          d[i] = *reinterpret_cast<const uint32_t*>(&sh.stage[16 * kk + 4 * g + i][64 * cq + 4 * r16]);
         const uint32_t p01a = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);  // d0[0] d1[0] d0[1] d1[1]
         const uint32_t p23a = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
         const uint32_t p01b = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);  // d0[2] d1[2] d0[3] d1[3]
@@ -282,9 +288,8 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
   };
   // two register buffers named statically (a copy between them would wait for loads in flight): step
   // st + 1's rows load while step st computes.  The loads are unconditional (a step past the end reads
-  // slot 0 and is never used) so that the compiler's counter waits stay exact.  The stage alternates
-  // between two buffers, so the next step's rows never overwrite rows still being read; barriers (A)
-  // and (B) order the rest.
+  // slot 0 and is never used) so that the compiler's counter waits stay exact.  Barriers (A) and (B)
+  // order the LDS traffic.
   const int nsteps = (n + 63) / 64;
   StepRows ra, rb;
   load_step(0, ra);
@@ -293,11 +298,11 @@ __global__ __launch_bounds__(kPthThreads) void pth_decode_kernel(PthDecodeArgs a
   for (int st = 0; st < nsteps; st += 2) {
     load_step(st + 1, rb);
     __builtin_amdgcn_sched_barrier(0);
-    compute_step(st, ra);
+    compute_step(ra);
     if (st + 1 >= nsteps) break;
     load_step(st + 2, ra);
     __builtin_amdgcn_sched_barrier(0);
-    compute_step(st + 1, rb);
+    compute_step(rb);
   }
 
   // ---- the normalized result of the wave's columns and the log-sum-exp
