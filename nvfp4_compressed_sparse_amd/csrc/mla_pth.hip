@@ -5,14 +5,15 @@
 //
 // pth_quant_kernel: one wave per token; lane l holds latent values 8l..8l+7 and rope value l.
 //
-// pth_decode_kernel: one 256-thread workgroup per (query token, group of 16 heads, split).  The split's
-// list entries are resolved to slots (order kept) in LDS; then, per step of 64 rows:
+// pth_decode_kernel: one 256-thread workgroup per (query token, group of 16 heads, split), two per
+// compute unit.  The split's list entries are resolved to slots (order kept) in LDS, and the heads'
+// latent q goes to LDS as f16; then, per step of 64 rows:
 //   * wave w scores rows 16w..16w+15 of the step for the 16 heads with MFMA 16x16x32: the latent part in
 //     f16 (q rounded to f16, the codes exact), the rope part in bf16 (both exact), one accumulator.  Lane
 //     l holds, for row l%16, the latent bytes 128(l/16)..+127 and rope dims 16(l/16)..+15, and in latent
 //     k-step ks feeds bytes 8ks..+7 of them (q's fragments use the same dimension order).  The scores
-//     (times the row's scale), the scales and the latent rows go to LDS; the next step's rows are already
-//     loading into a second register buffer;
+//     (times the row's scale) and the scales go to LDS, then, past the step's first barrier, the latent
+//     rows; the next step's rows are already loading into a second register buffer;
 //   * 16 threads per head take the step's softmax: the running max, P' = p * row scale (V's scale folded
 //     into P) as f16 in LDS, the running sum, the rescale factor;
 //   * wave w accumulates O += P' V for its 128 output columns over the step's 64 rows with MFMA
