@@ -181,20 +181,9 @@ __global__ __launch_bounds__(256) void index_logits_multi_kernel(IndexLogitsArgs
   const int b = blockIdx.x / a.chunks;
   const int T = a.T;
   float* wl = reinterpret_cast<float*>(lds + T * HI * kQRowBytes);
-  {  // the request's q (T*HI rows of 256 bytes, 16 per thread-load) and w into LDS
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * T * HI * kIdxDim);
-    for (int c = tid; c < T * HI * 16; c += 256) {
-      const int row = c >> 4, off = (c & 15) * 16;
-      *reinterpret_cast<u32x4*>(lds + row * kQRowBytes + off) = *reinterpret_cast<const u32x4*>(qsrc + row * 256 + off);
-    }
-    for (int c = tid; c < T * HI; c += 256) wl[c] = a.w[(int64_t)b * T * HI + c];
-  }
-  __syncthreads();
   const int pg_first = (blockIdx.x % a.chunks) * kIdxPagesPerWg + (tid >> 6) * kIdxPagesPerWave;
   const int L = a.ctx[b];
   const int p_end = L < a.ld ? L : (int)a.ld;
-  if (pg_first * 64 >= p_end) return;
-  const int n_pages = min(kIdxPagesPerWave, (p_end - pg_first * 64 + 63) / 64);
   // the wave's page-table entries, loaded once (lane j: page pg_first + j), as in index_logits_kernel
   const int pj = pg_first + (lane < kIdxPagesPerWave ? lane : 0);
   const int32_t tab = a.block_table[(int64_t)b * a.bt_stride + (pj < a.bt_stride ? pj : 0)];
@@ -204,10 +193,22 @@ __global__ __launch_bounds__(256) void index_logits_multi_kernel(IndexLogitsArgs
     ok = phys >= 0 && phys < a.num_pages;
     return a.pool + (ok ? phys : 0) * a.page_stride;
   };
-
+  // the first page's keys are requested before q is staged, so that the two loads overlap (a wave with
+  // no page reads page 0 or the pool's page 0 and leaves after the barrier)
   IndexPage buf[2];
   bool ok[2];
   load_index_page(page_base(0, ok[0]), r16, g, lane, buf[0]);
+  {  // the request's q (T*HI rows of 256 bytes, 16 per thread-load) and w into LDS
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * T * HI * kIdxDim);
+    for (int c = tid; c < T * HI * 16; c += 256) {
+      const int row = c >> 4, off = (c & 15) * 16;
+      *reinterpret_cast<u32x4*>(lds + row * kQRowBytes + off) = *reinterpret_cast<const u32x4*>(qsrc + row * 256 + off);
+    }
+    for (int c = tid; c < T * HI; c += 256) wl[c] = a.w[(int64_t)b * T * HI + c];
+  }
+  __syncthreads();
+  if (pg_first * 64 >= p_end) return;
+  const int n_pages = min(kIdxPagesPerWave, (p_end - pg_first * 64 + 63) / 64);
 #pragma unroll
   for (int i = 0; i < kIdxPagesPerWave; ++i) {
     if (i >= n_pages) break;
