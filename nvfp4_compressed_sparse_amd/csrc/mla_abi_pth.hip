@@ -18,11 +18,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Splits: enough workgroups to give every compute unit two (512, the decode kernel's occupancy), at
-// least 256 list entries each, and a chunk of at most kPthMaxChunk entries rounded up to whole 64-row
-// steps.
+// least 128 list entries (two 64-row steps) each, and a chunk of at most kPthMaxChunk entries rounded up
+// to whole 64-row steps.
 void pth_splits(int64_t units, int32_t topk, int32_t requested, int& S, int& chunk) {
   int64_t s = requested > 0 ? requested : ceil_div(512, units);
-  const int64_t cap = ceil_div(topk, 256);
+  const int64_t cap = ceil_div(topk, 128);
   if (requested <= 0 && s > cap) s = cap;
   if (s < 1) s = 1;
   int64_t c = ceil_div(ceil_div(topk, s), 64) * 64;
