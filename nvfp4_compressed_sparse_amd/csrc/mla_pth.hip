@@ -100,6 +100,15 @@ __global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArg
   const int lim = a.causal ? L - a.T + t : L - 1;
   const int64_t num_pages = a.num_slots / 64;
 
+  // the 16 heads' latent q, requested first so that it arrives during the list and page-table lookups:
+  // thread tid takes head tid / 16, dims 32 (tid % 16) .. +31
+  u32x4 qv[4];
+  {
+    const uint16_t* qsrc = a.q + (id * a.H + 16 * hg + (tid >> 4)) * 576 + 32 * (tid & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qsrc + 8 * j);
+  }
+
   // ---- this split's list entries -> slots, in list order
   const int e0 = s_idx * a.chunk;
   uint32_t slot_k[kPthEPT];
@@ -149,19 +158,16 @@ __global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArg
 #pragma unroll
   for (int k = 0; k < kPthEPT; ++k)
     if (vmask & (1u << k)) sh.slots[off++] = slot_k[k];
-  {  // the 16 heads' latent q to LDS as f16: thread tid takes head tid / 16, dims 32 (tid % 16) .. +31
-    const uint16_t* qsrc = a.q + (id * a.H + 16 * hg + (tid >> 4)) * 576 + 32 * (tid & 15);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qsrc + 8 * j);
-      f16x8 f;
+  for (int j = 0; j < 4; ++j) {  // the latent q to LDS as f16
+    const u32x4 v = qv[j];
+    f16x8 f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = (_Float16)bf16_to_f32(v[i] & 0xFFFFu);
-        f[2 * i + 1] = (_Float16)bf16_to_f32(v[i] >> 16);
-      }
-      *reinterpret_cast<f16x8*>(&sh.qs[tid >> 4][32 * (tid & 15) + 8 * j]) = f;
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = (_Float16)bf16_to_f32(v[i] & 0xFFFFu);
+      f[2 * i + 1] = (_Float16)bf16_to_f32(v[i] >> 16);
     }
+    *reinterpret_cast<f16x8*>(&sh.qs[tid >> 4][32 * (tid & 15) + 8 * j]) = f;
   }
   __syncthreads();
 
