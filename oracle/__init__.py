@@ -71,6 +71,8 @@ def _load():
         "mlo_kv_quant_nvfp4": (i64, [P, i64, P, i64, P, i64, P, i64, i64]),
         "mlo_kv_quant_fp8": (i64, [P, i64, P, i64, P, i64, P, i64, i64]),
         "mlo_sparse_decode": (i32, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, d, i32, P, i64, P, P, i32]),
+        "mlo_sparse_decode_fp8": (i32, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, d, i32, P, i64, P, P,
+                                        i32]),
         "mlo_dense_decode_fp8": (i32, [P, P, i64, i64, P, i64, P, i32, i32, i32, d, i32, P, i64, P, P, i32]),
         "mlo_merge_partials": (None, [P, P, i32, i32, P, P]),
         "mlo_stage_nvfp4_fp8": (None, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, i64, P, P]),
@@ -187,10 +189,12 @@ def kv_quant(fmt: str, k_nope: np.ndarray, k_rope: np.ndarray, slot_mapping: np.
 # --------------------------------------------------------------------------- attention
 
 def sparse_decode(q, pool, page_stride, num_pages, block_table, ctx, indices, sm_scale, causal=False, units=None,
-                  nthreads=0):
+                  nthreads=0, fmt="nvfp4"):
     """Sparse decode (launch post, native NVFP4 sparse MLA decode kernel): q bf16 bits [B,T,H,576];
     indices int32 [B,T,k] of logical positions (-1 = unused).  Returns (out [n,H,512], lse [n,H], threads)
-    in float64, n = B*T or len(units)."""
+    in float64, n = B*T or len(units).  fmt "nvfp4" reads 352-byte rows; "fp8" reads 576-byte FP8 rows
+    with the same selection rule (the FP8-cache arm of the launch post's native / staged / FP8
+    comparison)."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     B, T, H, D = q.shape
     assert D == QK
@@ -203,9 +207,11 @@ def sparse_decode(q, pool, page_stride, num_pages, block_table, ctx, indices, sm
     n = B * T if un is None else un.size
     out = np.empty((n, H, LATENT), np.float64)
     lse = np.empty((n, H), np.float64)
-    used = _load().mlo_sparse_decode(_ptr(q), _ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx),
-                                     _ptr(idx), B, T, H, k, float(sm_scale), int(bool(causal)), _ptr(un),
-                                     0 if un is None else un.size, _ptr(out), _ptr(lse), int(nthreads))
+    assert fmt in ("nvfp4", "fp8")
+    f = _load().mlo_sparse_decode if fmt == "nvfp4" else _load().mlo_sparse_decode_fp8
+    used = f(_ptr(q), _ptr(pool), page_stride, num_pages, _ptr(bt), bt.shape[1], _ptr(cx), _ptr(idx), B, T, H, k,
+             float(sm_scale), int(bool(causal)), _ptr(un), 0 if un is None else un.size, _ptr(out), _ptr(lse),
+             int(nthreads))
     return out, lse, used
 
 

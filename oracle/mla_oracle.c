@@ -292,15 +292,17 @@ static int set_threads(int nthreads) {
 #endif
 }
 
-/* Sparse decode.  q bf16 [B,T,H,576]; indices int32 [B,T,topk]; out double [n_units,H,512];
- * lse double [n_units,H].  units: optional list of query-token ids b*T+t to compute (NULL: all
- * B*T in order).  Returns the number of threads used. */
-int mlo_sparse_decode(const uint16_t* q, const uint8_t* pool, int64_t page_stride, int64_t num_pages,
-                      const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, const int32_t* indices,
-                      int B, int T, int H, int topk, double sm_scale, int causal, const int64_t* units,
-                      int64_t n_units, double* out, double* lse, int nthreads) {
+/* Sparse decode over one row format (0 = NVFP4 352-byte rows, 1 = FP8 576-byte rows).  q bf16
+ * [B,T,H,576]; indices int32 [B,T,topk]; out double [n_units,H,512]; lse double [n_units,H].  units:
+ * optional list of query-token ids b*T+t to compute (NULL: all B*T in order).  Returns the number of
+ * threads used. */
+static int sparse_decode_rows(int fmt, const uint16_t* q, const uint8_t* pool, int64_t page_stride, int64_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride, const int32_t* ctx,
+                              const int32_t* indices, int B, int T, int H, int topk, double sm_scale, int causal,
+                              const int64_t* units, int64_t n_units, double* out, double* lse, int nthreads) {
   int used = set_threads(nthreads);
   int64_t nq = units ? n_units : (int64_t)B * T;
+  int row_bytes = fmt == 0 ? NVFP4_ROW : FP8_ROW;
 #pragma omp parallel
   {
     double* K = (double*)malloc(sizeof(double) * QK * (topk > 0 ? topk : 1));
@@ -313,9 +315,11 @@ int mlo_sparse_decode(const uint16_t* q, const uint8_t* pool, int64_t page_strid
       const int32_t* idx = indices + id * topk;
       int64_t nrows = 0;
       for (int j = 0; j < topk; ++j) {
-        const uint8_t* row = row_address(pool, page_stride, num_pages, NVFP4_ROW, block_table, bt_stride, b,
+        const uint8_t* row = row_address(pool, page_stride, num_pages, row_bytes, block_table, bt_stride, b,
                                          idx[j], lim);
-        if (row) mlo_dequant_row_nvfp4(row, K + (nrows++) * QK);
+        if (!row) continue;
+        if (fmt == 0) mlo_dequant_row_nvfp4(row, K + (nrows++) * QK);
+        else mlo_dequant_row_fp8(row, K + (nrows++) * QK);
       }
       attend(q + id * H * QK, H, K, nrows, sm_scale, out + u * H * LATENT, lse + u * H, z);
     }
@@ -323,6 +327,27 @@ int mlo_sparse_decode(const uint16_t* q, const uint8_t* pool, int64_t page_strid
     free(z);
   }
   return used;
+}
+
+/* Sparse decode over NVFP4 rows (launch post, native NVFP4 sparse MLA decode kernel). */
+int mlo_sparse_decode(const uint16_t* q, const uint8_t* pool, int64_t page_stride, int64_t num_pages,
+                      const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, const int32_t* indices,
+                      int B, int T, int H, int topk, double sm_scale, int causal, const int64_t* units,
+                      int64_t n_units, double* out, double* lse, int nthreads) {
+  return sparse_decode_rows(0, q, pool, page_stride, num_pages, block_table, bt_stride, ctx, indices, B, T, H, topk,
+                            sm_scale, causal, units, n_units, out, lse, nthreads);
+}
+
+/* The same sparse decode over 576-byte FP8 rows: the third arm of the launch post's comparison (native
+ * NVFP4 / staged NVFP4 / FP8 attention over an FP8 cache, section "原生 NVFP4 稀疏 MLA 解码内核";
+ * analysis page, "A kernel that reads four bits directly").  Same selection rule; K = E4M3 values of the
+ * row (analysis page, row table: no per-row scale). */
+int mlo_sparse_decode_fp8(const uint16_t* q, const uint8_t* pool, int64_t page_stride, int64_t num_pages,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, const int32_t* indices,
+                          int B, int T, int H, int topk, double sm_scale, int causal, const int64_t* units,
+                          int64_t n_units, double* out, double* lse, int nthreads) {
+  return sparse_decode_rows(1, q, pool, page_stride, num_pages, block_table, bt_stride, ctx, indices, B, T, H, topk,
+                            sm_scale, causal, units, n_units, out, lse, nthreads);
 }
 
 /* Dense decode over an FP8 (576-byte row) cache: every position 0..limit is selected. */

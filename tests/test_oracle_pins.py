@@ -86,6 +86,119 @@ def test_pool_placement_rows_at_352_byte_stride():
     assert not pool[~written].any()
 
 
+def test_fp8_row_bytes_are_the_e4m3_casts_latent_then_rope():
+    """The 576-byte FP8 row (analysis page, row table: 512 latent + 64 rope values, no per-row scale) holds
+    torch's float8_e4m3fn cast of each value, saturated to +-448, latent first and rope after it: a row
+    written in another order, or with a scale, fails here.  Also its placement in a padded page."""
+    rng = np.random.default_rng(71)
+    mags = np.concatenate([rng.standard_normal(4000), rng.standard_normal(1000) * 600, rng.standard_normal(600) * 1e-3,
+                           [0.0, -0.0, 448.0, -449.0, 464.0, 1e30, -1e-30, 2.0 ** -10, 2.0 ** -9 * 3]])
+    vals = rng.permutation(np.resize(mags, 8 * 576)).astype(np.float32).reshape(8, 576)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)  # bf16 by truncation: exact bf16 inputs
+    exact = (bits.astype(np.uint32) << 16).view(np.float32)
+    ref = torch.from_numpy(exact).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for r in range(8):
+        row = oracle.quant_row_fp8(bits[r, :512], bits[r, 512:])
+        assert np.array_equal(row, ref[r]), f"row {r}: bytes {np.nonzero(row != ref[r])[0][:8]}"
+    page_stride = 64 * 576 + 32
+    pool = np.zeros(2 * page_stride, np.uint8)
+    assert oracle.kv_quant("fp8", bits[:3, :512], bits[:3, 512:], np.array([64 + 5, 2, -1], np.int64), pool,
+                           page_stride, 2) == 2
+    assert np.array_equal(pool[page_stride + 5 * 576:page_stride + 6 * 576], ref[0])
+    assert np.array_equal(pool[2 * 576:3 * 576], ref[1])
+    written = np.zeros(pool.size, bool)
+    written[page_stride + 5 * 576:page_stride + 6 * 576] = True
+    written[2 * 576:3 * 576] = True
+    assert not pool[~written].any()
+
+
+def _one_hot_pool(fmt, num_pages, value=1.5):
+    """A pool whose row in slot s has latent value `value` at column s % 512 and zeros elsewhere (rope 0).
+    1.5 is exact in every layout: NVFP4 block scale 0.25 with code 6, E4M3 1.5."""
+    n = num_pages * 64
+    lat = np.zeros((n, 512), np.float32)
+    lat[np.arange(n), np.arange(n) % 512] = value
+    lat_bits = (lat.view(np.uint32) >> 16).astype(np.uint16)
+    rope_bits = np.zeros((n, 64), np.uint16)
+    rb = 352 if fmt == "nvfp4" else 576
+    pool = np.zeros(num_pages * 64 * rb, np.uint8)
+    oracle.kv_quant(fmt, lat_bits, rope_bits, np.arange(n, dtype=np.int64), pool, 64 * rb, num_pages)
+    return pool, lat_bits, rope_bits
+
+
+def _selected_slot_counts(bt, ctx, idx, T, causal, num_pages):
+    """The selection rule restated: entry i of query token (b, t) counts iff 0 <= i <= limit and its page
+    entry bt[b][i // 64] lies in [0, num_pages); it stands for slot bt[b][i // 64] * 64 + i % 64."""
+    B = bt.shape[0]
+    counts = np.zeros((B * T, num_pages * 64), np.int64)
+    for b in range(B):
+        for t in range(T):
+            lim = int(ctx[b]) - T + t if causal else int(ctx[b]) - 1
+            for i in idx[b, t]:
+                i = int(i)
+                if i < 0 or i > lim or i // 64 >= bt.shape[1]:
+                    continue
+                pg = int(bt[b, i // 64])
+                if 0 <= pg < num_pages:
+                    counts[b * T + t, pg * 64 + i % 64] += 1
+    return counts
+
+
+def _selection_case():
+    """Two requests, shuffled multi-page tables with entries outside the pool, T = 2 causal, lists with -1
+    runs, positions past the limit, positions on bad pages and a duplicate."""
+    num_pages = 8
+    bt = np.array([[5, 2, 7, -1, 0], [3, 6, 1, 4, 9]], np.int32)  # 9 is outside the pool
+    ctx = np.array([250, 300], np.int32)
+    idx = np.array([[[3, 70, 130, 200, -1, 249, 64, 3, 10 ** 6, -7],
+                     [249, 248, 131, 1, -1, -1, 199, 192, 65, 100]],
+                    [[0, 63, 64, 299, 260, 257, 150, -1, 298, 129],
+                     [299, 298, 256, 5, 70, 140, 255, 200, 64, 63]]], np.int32)
+    return num_pages, bt, ctx, idx
+
+
+@pytest.mark.parametrize("decoder", ["nvfp4", "fp8", "dense_fp8", "pth"])
+def test_decoders_select_rows_through_the_page_table(decoder):
+    """With q = 0 every selected row weighs the same, so out = mean of the selected V rows; with one-hot
+    rows per slot the mean reveals exactly which slots were read and how often.  The expected multiset is
+    the selection rule applied by hand: a decoder that ignored the page table, the causal limit, the
+    -1 entries or duplicates would fail here."""
+    num_pages, bt, ctx, idx = _selection_case()
+    B, T, H = 2, 2, 4
+    q = np.zeros((B, T, H, 576), np.uint16)
+    if decoder == "dense_fp8":
+        idx = np.broadcast_to(np.arange(300, dtype=np.int32), (B, T, 300)).copy()
+    counts = _selected_slot_counts(bt, ctx, idx, T, True, num_pages)
+    expect = 1.5 * counts[:, :512] / np.maximum(counts.sum(1, keepdims=True), 1)
+    if decoder == "pth":
+        _, lat_bits, rope_bits = _one_hot_pool("fp8", num_pages)
+        n = num_pages * 64
+        lat_buf = np.zeros((n, 512), np.uint8)
+        sc_buf = np.zeros(n, np.float32)
+        rope_buf = np.zeros((n, 64), np.uint16)
+        oracle.kv_quant_pth(lat_bits, rope_bits, np.arange(n, dtype=np.int64), lat_buf, sc_buf, rope_buf)
+        out, lse, _ = oracle.sparse_decode_pth(q, lat_buf, sc_buf, rope_buf, bt, ctx, idx, 0.1, causal=True)
+        out = out.reshape(B * T, H, 512)
+        lse = lse.reshape(B * T, H)
+        tol = 1e-6  # the per-slot fp32 scale: 448 * fl(1.5 / 448) is 1.5 to fp32 precision
+    else:
+        fmt = "nvfp4" if decoder == "nvfp4" else "fp8"
+        pool, _, _ = _one_hot_pool(fmt, num_pages)
+        rb = 352 if fmt == "nvfp4" else 576
+        if decoder == "dense_fp8":
+            out, lse, _ = oracle.dense_decode_fp8(q, pool, 64 * rb, num_pages, bt, ctx, 0.1, causal=True)
+        else:
+            out, lse, _ = oracle.sparse_decode(q, pool, 64 * rb, num_pages, bt, ctx, idx, 0.1, causal=True, fmt=fmt)
+        tol = 1e-14
+    for u in range(B * T):
+        for h in range(H):
+            np.testing.assert_allclose(out[u, h], expect[u], rtol=tol, atol=tol)
+        # q = 0: every score is 0, so lse = ln |J|
+        assert np.allclose(lse[u], math.log(counts[u].sum()), atol=1e-12)
+    assert counts.sum(1).min() > 0
+    assert decoder == "dense_fp8" or (counts > 1).any()  # the sparse lists hold a duplicate
+
+
 def test_constants_from_pages():
     g = _golden("constants.json")
     # the printed softmax scale is 1/sqrt(192) (192 = 128 + 64) to the 7 digits shown
