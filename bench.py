@@ -183,10 +183,16 @@ def main():
     torch.cuda.empty_cache()
 
     q_sets, idx_sets = inp["q_sets"], inp["idx_sets"]
-    S = args.splits or (M.mla_sparse_decode_splits(cfg.B, cfg.T, cfg.H, cfg.topk) if cfg.topk else
-                        M.mla_dense_decode_splits(cfg.B, cfg.T, cfg.H, int(lay.ctx.max())))
+    sparse_fp8 = bool(cfg.topk) and cfg.fmt == "fp8"  # the FP8-cache arm of the pages' comparison
+    sparse_fn = M.mla_sparse_decode_fp8 if sparse_fp8 else M.mla_sparse_decode
     if cfg.topk:
-        ws_bytes = M.mla_sparse_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S)
+        S = args.splits or (M.mla_sparse_decode_fp8_splits if sparse_fp8 else M.mla_sparse_decode_splits)(
+            cfg.B, cfg.T, cfg.H, cfg.topk)
+    else:
+        S = args.splits or M.mla_dense_decode_splits(cfg.B, cfg.T, cfg.H, int(lay.ctx.max()))
+    if cfg.topk:
+        ws_bytes = (M.mla_sparse_decode_fp8_workspace_bytes if sparse_fp8 else M.mla_sparse_decode_workspace_bytes)(
+            cfg.B, cfg.T, cfg.H, cfg.topk, S)
     else:
         ws_bytes = M.mla_dense_decode_workspace_bytes(cfg.B, cfg.T, cfg.H, int(lay.ctx.max()), S)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # split counters start at zero
@@ -245,9 +251,8 @@ def main():
                                    st_pages * 64, cfg.sm_scale, num_splits=S, out=out1, lse=lse1, workspace=ws,
                                    stream=stream)
         elif cfg.topk:
-            M.mla_sparse_decode(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k],
-                                cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
-                                stream=stream)
+            sparse_fn(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k], cfg.sm_scale,
+                      causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=stream)
         else:
             M.mla_dense_decode_fp8(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], max_ctx,
                                    cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
@@ -306,7 +311,8 @@ def main():
         roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), timed "
                           "with HIP events on their stream")
     else:
-        roof["kernel"] = ("mla_sparse_decode" if cfg.topk else "mla_dense_decode_fp8") + " call: " + \
+        roof["kernel"] = (("mla_sparse_decode_fp8" if sparse_fp8 else "mla_sparse_decode") if cfg.topk
+                          else "mla_dense_decode_fp8") + " call: " + \
             ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
             " (split merge inside), timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
@@ -718,7 +724,8 @@ def run_cpu_baseline(cfg, cpu):
         oracle.kv_quant(cfg.fmt, cpu["new_lat"], cpu["new_rope"], wslots, scratch, cfg.page_stride, (n + 63) // 64)
         if cfg.topk:
             _, _, used = oracle.sparse_decode(cpu["q"], pool, cfg.page_stride, npg, bt, cpu["ctx"], cpu["idx"],
-                                              cfg.sm_scale, cfg.causal, units=cpu["units"], nthreads=nthreads)
+                                              cfg.sm_scale, cfg.causal, units=cpu["units"], nthreads=nthreads,
+                                              fmt=cfg.fmt)
         else:
             _, _, used = oracle.dense_decode_fp8(cpu["q"], pool, cfg.page_stride, npg, bt, cpu["ctx"], cfg.sm_scale,
                                                  cfg.causal, units=cpu["units"], nthreads=nthreads)

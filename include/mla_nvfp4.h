@@ -36,7 +36,14 @@
  *     [0, num_pages) are skipped by the writers; index entries < 0, beyond the query token's limit,
  *     or on a page-table entry outside [0, num_pages) are ignored by the decoders, as if absent.
  *   - bf16 arguments are IEEE bfloat16 bit patterns (uint16), non-finite inputs are outside the
- *     contract.
+ *     contract.  A decode query may hold any finite bf16 values: the matrix operands are FP16, and each
+ *     head's query is scaled by a power of two that brings its largest magnitude to [2^15, 2^16) before
+ *     the conversion (undone exactly in the score scale), so no element overflows and every element
+ *     within a factor 2^29 of the head's largest converts exactly.  The scores
+ *     sm_scale * <q, K_i> are accumulated in fp32: they must stay below 2^120 in magnitude, and their
+ *     absolute error grows with sm_scale * sum_d |q_d K_id| (about 2^-24 of it per term).
+ *   - A launch's grid must fit the dispatch limits: sizes whose grid would exceed 2^32 - 1 threads
+ *     return MLA_ERR_SHAPE (each entry point's limit follows from its grid, documented there).
  */
 #ifndef MLA_NVFP4_H
 #define MLA_NVFP4_H
@@ -81,7 +88,7 @@ const char* mla_status_string(int status);
  *   k_rope        (device) bf16 [n, 64], row r at k_rope + r*rope_stride elements; 16-byte aligned,
  *                 rope_stride a multiple of 8 and >= 64
  *   slot_mapping  (device) int64 [n]; token r is written to slot slot_mapping[r]; < 0 skips the token
- *   n             number of tokens, >= 0 (0 enqueues nothing)
+ *   n             number of tokens, 0 <= n < 2^26 (one 64-lane wave per token; 0 enqueues nothing)
  *   pool          (device) page pool, 16-byte aligned; page_stride_bytes >= 64*352, a multiple of 16
  *   num_pages     pages in the pool (> 0); slots on pages >= num_pages are skipped
  * Writes exactly 352 bytes per written token and nothing else.  Two tokens mapped to one slot race.
@@ -101,18 +108,20 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
  * launch post sizes its cooperating thread-block clusters by batch; here the selected rows of one
  * query token are split across workgroups instead). */
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
+int mla_sparse_decode_fp8_splits(int32_t B, int32_t T, int32_t H, int32_t topk);
 int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context);
 
-/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): one int32
- * arrival counter per query token and head group, then the FP16 partial outputs and fp32
+/* Workspace bytes a decode call with these arguments needs (0 when it runs unsplit): a fixed region of
+ * 65,536 int32 split arrival counters (one per query token and head group is used; a split launch with
+ * more query tokens x head groups returns MLA_ERR_SHAPE), then the FP16 partial outputs and fp32
  * log-sum-exps of the splits.  The last workgroup of a query token to finish merges its splits in the
  * same launch (the pages merge a cluster's partial results without a second launch either).
- * A workspace must be ZERO-FILLED before its first use; every call returns the counters to zero, so
- * a workspace can then be reused without refilling by later calls on the same stream with the same
- * B, T, H and split count.  A call of another shape may place its counters where an earlier call
- * wrote partial results: zero-fill the workspace again before such a call.  Two calls that can run
+ * A workspace must be ZERO-FILLED before its first use.  Every call returns the counters it used to
+ * zero, and no call writes partial results into the counter region, so a workspace can then be reused
+ * without refilling by later calls of any shape on the same stream.  Two calls that can run
  * concurrently must not share a workspace. */
 size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
+size_t mla_sparse_decode_fp8_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t max_context, int32_t num_splits);
 
 /*
@@ -131,7 +140,8 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *   context_lens  (device) int32 [B], tokens in each request's cache (the T query tokens included)
  *   indices       (device) int32 [B, T, topk] logical positions, -1 = unused
  *   B, T          >= 1;  H in {16, 32, 64, 128};  1 <= topk <= 2048
- *   sm_scale      > 0 and finite (the softmax scale, 1/sqrt(192) for the pages' model)
+ *   sm_scale      > 0, with sm_scale * log2(e) finite in fp32 (the softmax scale, 1/sqrt(192) for the
+ *                 pages' model)
  *   causal        0 or 1 (the T query tokens are the last T positions of the request)
  *   num_splits    0 = the library's choice, else 1..64: the selected rows of each query token are split
  *                 into this many parts whose results are merged with their log-sum-exp weights
@@ -139,12 +149,29 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *   lse           (device) fp32 [B, T, H] or NULL
  *   workspace     (device) >= mla_sparse_decode_workspace_bytes(...) bytes, 256-byte aligned, zero-filled
  *                 before its first use (see above); may be NULL when that size is 0
+ * The grid is B*T*(H/32 or 1 at H = 16)*S workgroups of 512 threads at 16 or 32 heads and B*T*S of 256 at
+ * 64 or 128; it must stay below 2^32 threads.
  */
 int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
                       const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
                       int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse MLA decode over 576-byte FP8 rows: the definition of mla_sparse_decode with K = the E4M3 values
+ * of the row (analysis page, row table: 512 latent + 64 rope bytes, no per-row scale), over a pool
+ * written by mla_kv_quant_fp8 (page_stride_bytes >= 64*576).  This is the third arm of the launch post's
+ * comparison (section "原生 NVFP4 稀疏 MLA 解码内核": native NVFP4, staged NVFP4, and FP8 attention over
+ * an FP8 cache; analysis page, "A kernel that reads four bits directly").  Arguments, workspace rules and
+ * errors as for mla_sparse_decode (its own split choice and workspace size, below); every H runs
+ * 512-thread workgroups of 16 or 32 heads, B*T*(H/32 or 1)*S of them.
+ */
+int mla_sparse_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                          const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                          int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Dense MLA decode over 576-byte FP8 rows: the same definition with J = {0, ..., limit} (every cached
@@ -175,8 +202,9 @@ int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_by
  *                      at byte ((id*P*64) + j) * 576; rows past its count are not written
  *   staged_block_table (device) int32 [B*T, P], written: entry id*P + p
  *   staged_lens        (device) int32 [B*T], written: the number of rows staged for query token id
- * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (sizes as for mla_sparse_decode), MLA_ERR_STRIDE_ALIGN,
- * MLA_ERR_DEVICE, MLA_ERR_HIP.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (sizes as for mla_sparse_decode; B*T below 2^20, so that up to 16
+ * workgroups of 256 threads per query token fit the dispatch limit), MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE,
+ * MLA_ERR_HIP.
  */
 int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num_pages, const int32_t* block_table,
                         int64_t bt_stride, const int32_t* context_lens, const int32_t* indices, int32_t B, int32_t T,
@@ -191,7 +219,7 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
  *     rope_i = bf16(rope_in_i / s) (nearest, ties to even; inf past the bf16 range).
  *   k_nope, k_rope    (device) bf16, k_nope 16-byte aligned with nope_stride a multiple of 8 (>= 512),
  *                     rope_stride >= 64 elements
- *   slot_mapping      (device) int64 [n]; slots < 0 or >= num_slots are skipped
+ *   slot_mapping      (device) int64 [n], 0 <= n < 2^26; slots < 0 or >= num_slots are skipped
  *   lat               (device) [num_slots, 512] bytes, 8-byte aligned; scale (device) fp32 [num_slots];
  *   rope              (device) bf16 [num_slots, 64]
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE, MLA_ERR_HIP.
@@ -204,11 +232,15 @@ int mla_kv_quant_pth(const void* k_nope, int64_t nope_stride, const void* k_rope
  * Sparse MLA decode over the per-token-head layout: the definition of mla_sparse_decode with position p of
  * request b at slot = block_table[b*bt_stride + p/64]*64 + p%64 (page entries in [0, num_slots/64)), and
  * K = (lat * scale, rope * scale), V = lat * scale (the inverse of the write).  Scores use FP16 latent
- * operands (q rounded to fp16, the codes exact) and bf16 rope operands (exact), accumulated in fp32.
+ * operands (each head's q scaled by a power of two into FP16's range as for mla_sparse_decode, then
+ * rounded to fp16; the codes exact) and bf16 rope operands (q's rope part scaled by the same power of two,
+ * exact), accumulated in fp32.
  *   lat, scale, rope, num_slots    as written by mla_kv_quant_pth (lat and rope 16-byte aligned)
  *   q, block_table, bt_stride, context_lens, indices, B, T, topk, sm_scale, causal, out, lse
  *                  as for mla_sparse_decode; H in {16, 32, 64, 128}
- *   num_splits     0 = the library's choice, else 1..64 (at most one split per 64 list entries)
+ *   num_splits     0 = the library's choice, else 1..64: the list is cut into chunks of ceil(topk / num_splits)
+ *                  entries rounded up to whole 64-entry steps, so ceil(topk / chunk) splits run, which may be
+ *                  fewer than requested (mla_sparse_decode_pth_workspace_bytes sizes for the same count)
  *   workspace      >= mla_sparse_decode_pth_workspace_bytes(...) bytes, 256-byte aligned (the splits' fp32
  *                  partial results; no zero-fill needed); may be NULL when that size is 0
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_STRIDE_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP.
@@ -234,7 +266,8 @@ int mla_sparse_decode_pth(const void* q, const void* lat, const float* scale, co
  *                      [0, num_pages) are skipped
  *   pool               (device) 16-byte aligned, page p at pool + p*page_stride_bytes
  *   page_stride_bytes  >= 8448, a multiple of 16
- * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (n < 0, num_pages < 1), MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE, MLA_ERR_HIP.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (n < 0 or n >= 2^26, num_pages < 1), MLA_ERR_STRIDE_ALIGN, MLA_ERR_DEVICE,
+ * MLA_ERR_HIP.
  */
 int mla_index_key_quant(const void* keys, int64_t key_stride, const int64_t* slot_mapping, int64_t n, void* pool,
                         int64_t page_stride_bytes, int64_t num_pages, void* stream);
@@ -284,8 +317,8 @@ int mla_index_logits(const void* q, const float* w, int32_t HI, const void* pool
  *              workspace can be reused without refilling by later calls on the same stream with the same n
  *              and ld (zero-fill it again before a call with another n or ld).  Concurrent calls must not
  *              share a workspace.
- * Errors: MLA_ERR_SHAPE (n < 0, k outside 1..2048, ld above 2^31-1, too many rows x chunks of 8192
- * positions), MLA_ERR_STRIDE_ALIGN (ld not a positive multiple of 4, misaligned pointers), MLA_ERR_NULL,
+ * Errors: MLA_ERR_SHAPE (n < 0, k outside 1..2048, ld above 2^31-1, n * ceil(ld / 8192) workgroups of 512
+ * threads past 2^32 - 1 threads), MLA_ERR_STRIDE_ALIGN (ld not a positive multiple of 4, misaligned pointers), MLA_ERR_NULL,
  * MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP.
  */
 size_t mla_index_topk_workspace_bytes(int64_t n, int64_t ld);

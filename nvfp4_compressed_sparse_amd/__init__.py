@@ -23,7 +23,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
+    "mla_sparse_decode", "mla_sparse_decode_fp8_splits", "mla_sparse_decode_fp8_workspace_bytes",
+    "mla_sparse_decode_fp8", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
     "mla_sparse_decode_pth_workspace_bytes", "mla_sparse_decode_pth", "mla_index_key_quant", "mla_index_logits",
     "mla_index_topk_workspace_bytes", "mla_index_topk",
 ]
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
                                              sz, P]),
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
+        "mla_sparse_decode_fp8_splits": (ctypes.c_int, [i32, i32, i32, i32]),
+        "mla_sparse_decode_fp8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "mla_sparse_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P, P,
+                                                 P, sz, P]),
         "mla_stage_nvfp4_fp8": (ctypes.c_int, [P, i64, i64, P, i64, P, P, i32, i32, i32, i32, P, P, P, P]),
         "mla_kv_quant_pth": (ctypes.c_int, [P, i64, P, i64, P, i64, P, P, P, i64, P]),
         "mla_sparse_decode_pth_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -187,9 +192,8 @@ def _common(q, pool, block_table, context_lens):
         raise ValueError("context_lens must be a contiguous [B] int32 tensor")
 
 
-def mla_sparse_decode(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,
-                      causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
-    """Sparse MLA decode over NVFP4 rows; returns (out [B,T,H,512] bf16, lse or None)."""
+def _sparse(fn, ws_fn, q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale, causal,
+            num_splits, out, lse, workspace, stream):
     import torch
     _common(q, pool, block_table, context_lens)
     _dev(indices, torch.int32, "indices")
@@ -197,16 +201,39 @@ def mla_sparse_decode(q, pool, page_stride_bytes, num_pages, block_table, contex
     if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, T) or not indices.is_contiguous():
         raise ValueError("indices must be a contiguous [B, T, topk] int32 tensor")
     topk = indices.shape[2]
-    ws = lib().mla_sparse_decode_workspace_bytes(B, T, H, topk, int(num_splits))
+    ws = getattr(lib(), ws_fn)(B, T, H, topk, int(num_splits))
     out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
-    st = lib().mla_sparse_decode(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
-                                 block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(),
-                                 indices.data_ptr(), B, T, H, topk, float(sm_scale), int(bool(causal)),
-                                 int(num_splits), out.data_ptr(), None if lse is None else lse.data_ptr(),
-                                 None if workspace is None else workspace.data_ptr(),
-                                 0 if workspace is None else workspace.numel(), _stream(stream))
-    _check("mla_sparse_decode", st)
+    st = getattr(lib(), fn)(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+                            block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), indices.data_ptr(),
+                            B, T, H, topk, float(sm_scale), int(bool(causal)), int(num_splits), out.data_ptr(),
+                            None if lse is None else lse.data_ptr(), None if workspace is None else workspace.data_ptr(),
+                            0 if workspace is None else workspace.numel(), _stream(stream))
+    _check(fn, st)
     return out, lse
+
+
+def mla_sparse_decode(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,
+                      causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Sparse MLA decode over NVFP4 rows; returns (out [B,T,H,512] bf16, lse or None)."""
+    return _sparse("mla_sparse_decode", "mla_sparse_decode_workspace_bytes", q, pool, page_stride_bytes, num_pages,
+                   block_table, context_lens, indices, sm_scale, causal, num_splits, out, lse, workspace, stream)
+
+
+def mla_sparse_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,
+                          causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Sparse MLA decode over 576-byte FP8 rows (the FP8-cache arm of the pages' comparison); returns
+    (out [B,T,H,512] bf16, lse or None)."""
+    return _sparse("mla_sparse_decode_fp8", "mla_sparse_decode_fp8_workspace_bytes", q, pool, page_stride_bytes,
+                   num_pages, block_table, context_lens, indices, sm_scale, causal, num_splits, out, lse, workspace,
+                   stream)
+
+
+def mla_sparse_decode_fp8_splits(B, T, H, topk):
+    return lib().mla_sparse_decode_fp8_splits(B, T, H, topk)
+
+
+def mla_sparse_decode_fp8_workspace_bytes(B, T, H, topk, num_splits=0):
+    return lib().mla_sparse_decode_fp8_workspace_bytes(B, T, H, topk, num_splits)
 
 
 def mla_dense_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, context_lens, max_context, sm_scale,

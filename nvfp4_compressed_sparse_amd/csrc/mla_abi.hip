@@ -74,9 +74,11 @@ int auto_splits_wide(int64_t units, int64_t entries) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout when S > 1: [split arrival counters: B*T*head groups int32][partial outputs:
-// B*T*H*S*512 fp16][partial lse: B*T*H*S fp32], each region 256-byte aligned.  The counters must be
-// zero before the first call; every call leaves them zero.
+// Workspace layout when S > 1: [split arrival counters: a fixed region of kMaxSplitCounters int32, of
+// which B*T*head groups are used][partial outputs: B*T*H*S*512 fp16][partial lse: B*T*H*S fp32], each
+// region 256-byte aligned.  The counters must be zero before the first call; every call leaves them
+// zero, and since the counter region is the same for every shape, later calls of any shape may reuse
+// the workspace.
 struct WsLayout {
   size_t cnt_off, o_off, lse_off, total;
 };
@@ -85,11 +87,21 @@ WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
   WsLayout l{0, 0, 0, 0};
   if (S <= 1) return l;
   const size_t rows = (size_t)(B * T * H);
-  const size_t units = (size_t)(B * T * head_groups((int32_t)H));
-  l.o_off = round256(units * sizeof(int32_t));
+  l.o_off = round256((size_t)mla::kMaxSplitCounters * sizeof(int32_t));
   l.lse_off = l.o_off + round256(rows * (size_t)S * 512 * sizeof(uint16_t));
   l.total = l.lse_off + round256(rows * (size_t)S * sizeof(float));
   return l;
+}
+
+// The decode launch for these sizes stays inside the dispatch limits: its grid, in threads, fits 32 bits,
+// and a split launch has at most kMaxSplitCounters arrival counters.
+bool decode_launch_fits(int fmt, int64_t B, int64_t T, int32_t H, int S, bool sparse) {
+  const bool wide = sparse && mla::uses_wide_kernel(fmt, H);
+  const int64_t units = wide ? B * T : B * T * head_groups(H);
+  const int64_t threads = wide ? mla::kWideDecodeThreads : mla::kDecodeThreads;
+  if (units * S * threads > mla::kMaxLaunchThreads) return false;
+  if (S > 1 && units > mla::kMaxSplitCounters) return false;
+  return true;
 }
 
 size_t workspace_for(int64_t B, int64_t T, int64_t H, int S) { return workspace_layout(B, T, H, S).total; }
@@ -100,7 +112,7 @@ int check_quant(const void* k_nope, int64_t nope_stride, const void* k_rope, int
   if (n < 0) return MLA_ERR_SHAPE;
   if (n == 0) return MLA_OK;
   if (!k_nope || !k_rope || !slot_mapping || !pool) return MLA_ERR_NULL;
-  if (num_pages <= 0) return MLA_ERR_SHAPE;
+  if (num_pages <= 0 || n > mla::kMaxWriteTokens) return MLA_ERR_SHAPE;
   if (nope_stride < 512 || rope_stride < 64 || nope_stride % 8 || rope_stride % 8) return MLA_ERR_STRIDE_ALIGN;
   if (!aligned(k_nope, 16) || !aligned(k_rope, 16) || !aligned(pool, 16) || !aligned(slot_mapping, 8))
     return MLA_ERR_STRIDE_ALIGN;
@@ -126,7 +138,8 @@ int check_decode_common(const void* q, const void* pool, int64_t page_stride, in
   if (!q || !pool || !block_table || !ctx || !out) return MLA_ERR_NULL;
   if (B < 1 || T < 1 || !valid_heads(H) || num_pages < 1 || bt_stride < 1) return MLA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
-  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return MLA_ERR_SHAPE;  // a softmax scale: positive, finite
+  // a softmax scale: positive, and finite also in base 2 (times log2 e)
+  if (!(sm_scale > 0.0f) || !(sm_scale * 1.4426950408889634f < INFINITY)) return MLA_ERR_SHAPE;
   if ((int64_t)B * T * H * 576 > ((int64_t)1 << 40)) return MLA_ERR_SHAPE;
   if (page_stride < 64LL * row_bytes || page_stride % 16) return MLA_ERR_STRIDE_ALIGN;
   // row addresses travel as 32-bit multiples of 16 bytes
@@ -145,6 +158,7 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   // a dense split starts on a page boundary, so that each 64-row step of the decoder is one page
   if (!indices) chunk = (int)ceil_div(chunk, 64) * 64;
   if (chunk > kMaxChunk) return MLA_ERR_SHAPE;
+  if (!decode_launch_fits(fmt, B, T, H, S, indices != nullptr)) return MLA_ERR_SHAPE;
   size_t need = workspace_for(B, T, H, S);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
@@ -221,6 +235,11 @@ int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk) {
   return auto_splits((int64_t)B * T * head_groups(H), topk, 1);
 }
 
+int mla_sparse_decode_fp8_splits(int32_t B, int32_t T, int32_t H, int32_t topk) {
+  if (B < 1 || T < 1 || !valid_heads(H) || topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  return auto_splits((int64_t)B * T * head_groups(H), topk, 1);
+}
+
 int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context) {
   if (B < 1 || T < 1 || !valid_heads(H) || max_context < 1) return 0;
   return auto_splits((int64_t)B * T * head_groups(H), max_context, ceil_div(max_context, kMaxChunk));
@@ -228,6 +247,12 @@ int mla_dense_decode_splits(int32_t B, int32_t T, int32_t H, int32_t max_context
 
 size_t mla_sparse_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
   int S = num_splits > 0 ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
+  if (S < 1) return 0;
+  return workspace_for(B, T, H, S);
+}
+
+size_t mla_sparse_decode_fp8_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
+  int S = num_splits > 0 ? num_splits : mla_sparse_decode_fp8_splits(B, T, H, topk);
   if (S < 1) return 0;
   return workspace_for(B, T, H, S);
 }
@@ -255,6 +280,23 @@ int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes
                     topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
 }
 
+int mla_sparse_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                          const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                          int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, B, T, H,
+                               sm_scale, causal, out, MLA_FP8_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (!indices) return MLA_ERR_NULL;
+  if (!aligned(indices, 4)) return MLA_ERR_STRIDE_ALIGN;
+  if (topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_SHAPE;
+  int S = num_splits ? num_splits : mla_sparse_decode_fp8_splits(B, T, H, topk);
+  return run_decode(1, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
+                    topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
 int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
                          const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens, int32_t B,
                          int32_t T, int32_t H, int32_t max_context, float sm_scale, int32_t causal, int32_t num_splits,
@@ -277,7 +319,10 @@ int mla_stage_nvfp4_fp8(const void* pool, int64_t page_stride_bytes, int64_t num
     return MLA_ERR_NULL;
   if (B < 1 || T < 1 || topk < 1 || topk > MLA_MAX_TOPK || num_pages < 1 || bt_stride < 1) return MLA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
-  if ((int64_t)B * T > ((int64_t)1 << 31) / 64) return MLA_ERR_SHAPE;
+  // staged rows are addressed with 32-bit row counts, and the launch (at most 16 workgroups of 256
+  // threads per query token) must fit the dispatch limit
+  if ((int64_t)B * T > ((int64_t)1 << 31) / 64 || (int64_t)B * T * 16 * 256 > mla::kMaxLaunchThreads)
+    return MLA_ERR_SHAPE;
   if (page_stride_bytes < 64LL * MLA_NVFP4_ROW_BYTES || page_stride_bytes % 16) return MLA_ERR_STRIDE_ALIGN;
   // row addresses travel as 32-bit multiples of 16 bytes
   if ((num_pages * page_stride_bytes) / 16 > (int64_t)0xFFFFFFFFLL) return MLA_ERR_SHAPE;

@@ -47,7 +47,7 @@ int mla_index_key_quant(const void* keys, int64_t key_stride, const int64_t* slo
   if (key_stride < 128 || key_stride % 2) return MLA_ERR_STRIDE_ALIGN;
   if (page_stride_bytes < mla::kIndexPageBytes || page_stride_bytes % 16) return MLA_ERR_STRIDE_ALIGN;
   if (!aligned(keys, 4) || !aligned(slot_mapping, 8) || !aligned(pool, 16)) return MLA_ERR_STRIDE_ALIGN;
-  if (n > ((int64_t)1 << 33)) return MLA_ERR_SHAPE;
+  if (n > mla::kMaxWriteTokens) return MLA_ERR_SHAPE;
   int st = check_device();
   if (st != MLA_OK) return st;
   mla::IndexKeyArgs a{(const uint16_t*)keys, key_stride, slot_mapping, n, (uint8_t*)pool, page_stride_bytes, num_pages};
@@ -68,7 +68,7 @@ int mla_index_logits(const void* q, const float* w, int32_t HI, const void* pool
       !aligned(context_lens, 4) || !aligned(logits, 4))
     return MLA_ERR_STRIDE_ALIGN;
   const int64_t chunks = ceil_div(ceil_div(max_context, 64), mla::kIdxPagesPerWg);
-  if ((int64_t)B * chunks > INT32_MAX) return MLA_ERR_SHAPE;
+  if ((int64_t)B * chunks * 256 > mla::kMaxLaunchThreads) return MLA_ERR_SHAPE;  // 256-thread workgroups
   int st = check_device();
   if (st != MLA_OK) return st;
   mla::IndexLogitsArgs a;
@@ -98,7 +98,8 @@ int mla_index_topk(const float* logits, int64_t ld, const int32_t* lengths, int6
   if (ld < 4 || ld % 4) return MLA_ERR_STRIDE_ALIGN;
   if (ld > INT32_MAX) return MLA_ERR_SHAPE;  // positions are int32
   const int64_t chunks = ceil_div(ld, mla::kTopkChunk);
-  if (n * chunks > INT32_MAX) return MLA_ERR_SHAPE;  // one workgroup per chunk of every row
+  // one workgroup of kTopkThreads per chunk of every row: the grid, in threads, fits the dispatch limit
+  if (n * chunks * mla::kTopkThreads > mla::kMaxLaunchThreads) return MLA_ERR_SHAPE;
   if (n == 0) return MLA_OK;
   if (!logits || !lengths || !out || !workspace) return MLA_ERR_NULL;
   if (!aligned(logits, 16) || !aligned(lengths, 4) || !aligned(out, 4) || !aligned(workspace, 256))

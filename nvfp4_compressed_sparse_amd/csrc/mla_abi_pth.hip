@@ -19,7 +19,8 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Splits: enough workgroups to give every compute unit two (512, the decode kernel's occupancy), at
 // least 128 list entries (two 64-row steps) each, and a chunk of at most kPthMaxChunk entries rounded up
-// to whole 64-row steps.
+// to whole 64-row steps.  A requested count sets the chunk, ceil(topk / requested) rounded up to whole
+// steps, so the effective count S = ceil(topk / chunk) may be lower than the request.
 void pth_splits(int64_t units, int32_t topk, int32_t requested, int& S, int& chunk) {
   int64_t s = requested > 0 ? requested : ceil_div(512, units);
   const int64_t cap = ceil_div(topk, 128);
@@ -46,7 +47,7 @@ int mla_kv_quant_pth(const void* k_nope, int64_t nope_stride, const void* k_rope
   if (n < 0) return MLA_ERR_SHAPE;
   if (n == 0) return MLA_OK;
   if (!k_nope || !k_rope || !slot_mapping || !lat || !scale || !rope) return MLA_ERR_NULL;
-  if (num_slots < 1 || n > ((int64_t)1 << 33)) return MLA_ERR_SHAPE;
+  if (num_slots < 1 || n > mla::kMaxWriteTokens) return MLA_ERR_SHAPE;
   if (nope_stride < 512 || rope_stride < 64 || nope_stride % 8) return MLA_ERR_STRIDE_ALIGN;
   if (!aligned(k_nope, 16) || !aligned(k_rope, 2) || !aligned(slot_mapping, 8) || !aligned(lat, 8) ||
       !aligned(scale, 4) || !aligned(rope, 2))
@@ -75,7 +76,7 @@ int mla_sparse_decode_pth(const void* q, const void* lat, const float* scale, co
   if (H != 16 && H != 32 && H != 64 && H != 128) return MLA_ERR_SHAPE;
   if (topk < 1 || topk > MLA_MAX_TOPK || num_splits < 0 || num_splits > 64) return MLA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return MLA_ERR_SHAPE;
-  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return MLA_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !(sm_scale * 1.4426950408889634f < INFINITY)) return MLA_ERR_SHAPE;
   if ((int64_t)B * T * H * 576 > ((int64_t)1 << 40)) return MLA_ERR_SHAPE;
   if (num_slots > ((int64_t)1 << 32)) return MLA_ERR_SHAPE;  // slots travel as 32-bit values
   if (!aligned(q, 16) || !aligned(lat, 16) || !aligned(scale, 4) || !aligned(rope, 16) || !aligned(block_table, 4) ||
@@ -83,8 +84,11 @@ int mla_sparse_decode_pth(const void* q, const void* lat, const float* scale, co
     return MLA_ERR_STRIDE_ALIGN;
   int S, chunk;
   pth_splits((int64_t)B * T * (H / 16), topk, num_splits, S, chunk);
-  if (num_splits > 0 && S != num_splits) return MLA_ERR_SHAPE;  // more splits than 64-row steps
   const int64_t rows = (int64_t)B * T * H;
+  // the decode grid (256-thread workgroups) and the merge grid (128 threads per head row) fit the
+  // dispatch limit
+  if ((int64_t)B * T * (H / 16) * S * 256 > mla::kMaxLaunchThreads || rows * 128 > mla::kMaxLaunchThreads)
+    return MLA_ERR_SHAPE;
   const size_t need = pth_workspace(rows, S);
   if (need) {
     if (!workspace) return MLA_ERR_NULL;

@@ -5,8 +5,9 @@
 // and head, softmax attention of the 576-wide absorbed query over the selected cached rows, with the
 // 512-value latent as V; only the selected compressed rows are loaded and they are unpacked on chip;
 // accumulation is FP32.  As in the pages' kernel the matrix operands are FP16: every dequantized K/V
-// value is exact in FP16, a bf16 query element converts exactly when its magnitude is in FP16's normal
-// range, and P rounds to FP16.
+// value is exact in FP16; each head's bf16 query is first scaled by a power of two that brings its
+// largest magnitude to [2^15, 2^16) (undone, exactly, in the score scale), so any finite bf16 query
+// converts without overflow; P rounds to FP16.
 //
 // Work decomposition: one 512-thread workgroup (8 wavefronts, two per SIMD) per compute unit.
 //   * workgroup = (query token, head group of 16*HT heads, split s of the token's position list);
@@ -43,7 +44,7 @@
 
 namespace mla {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStepRows = 64;
 constexpr int kMaxChunk = 2048;        // list entries one workgroup holds
@@ -59,8 +60,9 @@ constexpr int kHeadStart = 2;                  // of those, steps gathered befor
 // takes one 16-byte chunk more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes
 // of a lane group start on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l
 // of a wave's DMA load u fills LDS chunk 64u+l of the wave's 16 rows; the padding chunks are not
-// loaded.  A step's slot is reused NS steps later; step k is issued during step k-(NS-2).
-template <int FMT>
+// loaded.  A step's slot is reused NS steps later; step k is issued during step k-(NS-2).  Sparse FP8
+// lists keep three slots: with the row list beside it, a fourth 37 KB slot would not fit in LDS.
+template <int FMT, bool DENSE>
 struct Geo {
   static constexpr int kRowBytes = FMT == 0 ? kNvfp4Row : kFp8Row;
   static constexpr int kChunks = kRowBytes / 16;                 // 22 or 36 per row
@@ -70,7 +72,7 @@ struct Geo {
   static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 6 or 10 DMA loads per wave per step
   static_assert((kLoads - 1) * 64 < kWaveChunks, "only a wave's last gather load is partial");
   static constexpr int kSlot = kStepRows * kStride;              // bytes of one step
-  static constexpr int kSlots = FMT == 0 ? 6 : 4;                // ring depth
+  static constexpr int kSlots = FMT == 0 ? 6 : (DENSE ? 4 : 3);  // ring depth
   static constexpr int kRing = kSlots * kSlot;
 };
 
@@ -91,7 +93,7 @@ __device__ __forceinline__ void write_p(uint8_t* prow, int rt, int g, const floa
 // split (64-aligned, so that each step is one page) keeps its page-table entries instead.
 template <int FMT, int NH, bool DENSE>
 struct Shared {
-  uint8_t ring[Geo<FMT>::kRing];
+  uint8_t ring[Geo<FMT, DENSE>::kRing];
   uint8_t ptile[2][NH * kPStride];             // P of steps k (even/odd): [head][row], FP16
   uint32_t rowlist[DENSE ? 1 : kMaxChunk];     // sparse: row addresses of the split's valid entries
   int pages[DENSE ? kMaxChunk / kStepRows : 1];  // dense: page of each step, -1 = not in the pool
@@ -113,7 +115,7 @@ __device__ __forceinline__ void raise_reference(const float (&smax)[NH][4], int 
   for (int tt = 0; tt < HT; ++tt) {
     const int h = 16 * tt + n;
     const float ms = fmaxf(fmaxf(smax[h][0], smax[h][1]), fmaxf(smax[h][2], smax[h][3]));
-    const float rnew = ms > ref[tt] + kLazyRescale ? ms : ref[tt];
+    const float rnew = ms - ref[tt] > kLazyRescale ? ms : ref[tt];
     alpha[tt] = ref[tt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ref[tt] - rnew);
     ref[tt] = rnew;
   }
@@ -121,7 +123,7 @@ __device__ __forceinline__ void raise_reference(const float (&smax)[NH][4], int 
 
 template <int HT, int FMT, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
-  using G = Geo<FMT>;
+  using G = Geo<FMT, DENSE>;
   constexpr int ROWB = G::kRowBytes;
   constexpr int RS = G::kStride;
   constexpr int NL = G::kLoads;
@@ -378,22 +380,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
     issue_upto(kEarly - 1);
     // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
-    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17)
+    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17); the four lane groups together hold
+    // the head's 576 values.  Each head is scaled by its power of two 2^kq (largest magnitude to
+    // [2^15, 2^16)), and its score scale by 2^-kq.
     f16x8 qf[HT][18];
+    float sl2h[HT];  // softmax scale * log2(e) * 2^-kq of head 16tt+n
 #pragma unroll
-    for (int tt = 0; tt < HT; ++tt)
+    for (int tt = 0; tt < HT; ++tt) {
+      auto qword = [&](int ks) {
+        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
+        return *reinterpret_cast<const u32x4*>(qstage + 2 * ((16 * tt + n) * kQK + d));
+      };
+      uint32_t mq = 0;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qstage + 2 * ((16 * tt + n) * kQK + d));
-        f16x2 hv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t dd = raw[k];
-          hv[k] = f16x2{(_Float16)__uint_as_float(dd << 16), (_Float16)__uint_as_float(dd & 0xFFFF0000u)};
-        }
-        qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
+        const uint32_t m = bf16x8_max_mag(qword(ks));
+        mq = mq > m ? mq : m;
       }
+      const int kq = q_shift(group4_max_u32(mq));
+      sl2h[tt] = __builtin_ldexpf(a.scale_log2, -kq);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const u32x4 raw = qword(ks);
+        qf[tt][ks] = as_f16x8(bf16x2_pow2_to_f16x2(raw[0], kq), bf16x2_pow2_to_f16x2(raw[1], kq),
+                              bf16x2_pow2_to_f16x2(raw[2], kq), bf16x2_pow2_to_f16x2(raw[3], kq));
+      }
+    }
     issue_upto(kFirst - 1);
     wait_for_step(0);
     lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
     for (int k = 0; k <= nsteps; ++k) {
       issue_upto(k + NS - 2);  // up to the slot of step k-2 (fully consumed)
-      float sv[HT][4];  // raw scores (before the softmax scale); masked rows -inf
+      float sv[HT][4];  // scores times the head's scale (base 2); masked rows -inf
       float psum[HT];   // sum of this lane's speculative P per head tile
       if (k < nsteps) {
         const uint8_t* rr = slot_ptr(k) + (16 * rt + n) * RS;
@@ -451,7 +463,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         // scores of rows 16rt+4g+i, heads 16tt+n; base-2 maxima; speculative P = 2^(scale*s - ref) with
         // the current ref.  Only the last step can hold rows past the list (its padding): masked -inf.
-        const float sl2 = a.scale_log2;
+        // The scaled score is rounded once (no fused multiply-add) and both the maxima and P use that
+        // rounded value, and the reference test compares a difference: so P <= 2^8 holds exactly even
+        // where scores are large enough for an added 8 to round away.
         const int rbase = k * kStepRows + 16 * rt + 4 * g;
         // (dense: a step whose page is not in the pool selects nothing)
         const bool page_ok = !DENSE || sh.pages[DENSE ? k : 0] >= 0;
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[tt][i] = acc[tt][i];
+          for (int i = 0; i < 4; ++i) sv[tt][i] = __fmul_rn(acc[tt][i], sl2h[tt]);
         if (!full) {
 #pragma unroll
           for (int tt = 0; tt < HT; ++tt)
@@ -471,12 +485,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int tt = 0; tt < HT; ++tt) {
-          mxs[tt] = max4(sv[tt][0], sv[tt][1], sv[tt][2], sv[tt][3]) * sl2;
-          raise |= mxs[tt] > ref[tt] + kLazyRescale;
+          mxs[tt] = max4(sv[tt][0], sv[tt][1], sv[tt][2], sv[tt][3]);
+          raise |= mxs[tt] - ref[tt] > kLazyRescale;
           const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][i], sl2, -mr));
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
           psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
           write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
         }
@@ -495,14 +509,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         if (sh.flag[k & 1]) {  // rare: the reference rises; every wave takes this branch
           float alpha[HT];
           raise_reference<HT, NH>(sh.smax[k & 1], n, ref, alpha);
-          const float sl2 = a.scale_log2;
 #pragma unroll
           for (int tt = 0; tt < HT; ++tt) {
             lsum[tt] *= alpha[tt];
             const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[tt][i], sl2, -mr));
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
             psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
             write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
           }
@@ -709,14 +722,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     if (tid == 0) sh.last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
     if (sh.last) {
-      // running merge: the own split from LDS, then the others four per round with every load of a
-      // round (results and lse) issued together
-      float M = sh.tile_lse[h];
-      float Z = M == -INFINITY ? 0.0f : 1.0f;
+      // running merge over the splits in their order, four per round with every load of a round (results
+      // and lse) issued together; this workgroup's own split comes from LDS, rounded to FP16 as the
+      // stored ones are, so the merged bits do not depend on which split's workgroup merges
+      float M = -INFINITY;
+      float Z = 0.0f;
       f32x4 acc[NQ];
 #pragma unroll
-      for (int jj = 0; jj < NQ; ++jj)
-        acc[jj] = M == -INFINITY ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const f32x4*>(own + 4 * TPH * jj);
+      for (int jj = 0; jj < NQ; ++jj) acc[jj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const float* pl = a.part_lse + hrow * S;
       for (int k0 = 0; k0 < S; k0 += 4) {
         float lk[4];
@@ -725,7 +738,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int u = 0; u < 4; ++u) {
           const int k = k0 + u;
           lk[u] = -INFINITY;
-          if (k >= S || k == s) continue;
+          if (k >= S) continue;
+          if (k == s) {
+            lk[u] = sh.tile_lse[h];
+#pragma unroll
+            for (int jj = 0; jj < NQ; ++jj) raw[u][jj] = pack_h4(*reinterpret_cast<const f32x4*>(own + 4 * TPH * jj));
+            continue;
+          }
           lk[u] = load_coherent(pl + k);
           const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent + c4);
 #pragma unroll
@@ -771,14 +790,17 @@ static void launch_one(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream) {
   const bool dense = a.indices == nullptr;
-  if (uses_wide_kernel(fmt, a.H)) return launch_decode_wide(fmt, a, stream);
+  if (uses_wide_kernel(fmt, a.H) && !dense) return launch_decode_wide(fmt, a, stream);
   if (fmt == 0) {
+    if (dense) return hipErrorInvalidValue;
     if (a.H == 16) launch_one<1, 0, false>(a, stream);
     else launch_one<2, 0, false>(a, stream);
-  } else {
-    if (!dense) return hipErrorInvalidValue;
+  } else if (dense) {
     if (a.H == 16) launch_one<1, 1, true>(a, stream);
     else launch_one<2, 1, true>(a, stream);
+  } else {
+    if (a.H == 16) launch_one<1, 1, false>(a, stream);
+    else launch_one<2, 1, false>(a, stream);
   }
   return hipGetLastError();
 }

@@ -4,7 +4,8 @@
 // What it computes is the same as the 16/32-head kernel (launch post, section "原生 NVFP4 稀疏 MLA 解码
 // 内核" (native NVFP4 sparse MLA decode kernel); the analysis page, section "A kernel that reads four
 // bits directly"): softmax attention of each head's 576-wide absorbed query over the selected cached
-// rows, with the 512-value latent as V, FP16 matrix operands and FP32 accumulation.  With 128 heads
+// rows, with the 512-value latent as V, FP16 matrix operands and FP32 accumulation (each head's query
+// scaled by a power of two into FP16's range, undone exactly in the score scale).  With 128 heads
 // the work per row is large enough for the matrix cores to be the bound, so the design differs from
 // the pages' memory-bound kernel: one row is shared by far more MFMA work than its dequantization.
 //
@@ -29,7 +30,7 @@ namespace mla {
 
 namespace {
 
-constexpr int kWThreads = 256;
+constexpr int kWThreads = kWideDecodeThreads;
 constexpr int kWWaves = kWThreads / 64;
 constexpr int kWStep = 32;                       // rows per step
 constexpr int kWMaxChunk = 2048;                 // list entries one workgroup holds
@@ -339,19 +340,27 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
     *reinterpret_cast<f16x8*>(sh.vtile + (8 * co + c) * kVStride + 16 * Gq) = as_f16x8(v[0], v[1], v[2], v[3]);
   };
 
+  // FP16 query fragments: each head scaled by its power of two 2^kq (largest magnitude to [2^15, 2^16),
+  // the four lane groups together hold the head's 576 values), its score scale by 2^-kq
   f16x8 qf[HT][18];
+  float sl2h[HT];  // softmax scale * log2(e) * 2^-kq of head hw0+16tt+n
 #pragma unroll
-  for (int tt = 0; tt < HT; ++tt)
+  for (int tt = 0; tt < HT; ++tt) {
+    uint32_t mq = 0;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      f16x2 hv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t dd = qraw[tt][ks][k];
-        hv[k] = f16x2{(_Float16)__uint_as_float(dd << 16), (_Float16)__uint_as_float(dd & 0xFFFF0000u)};
-      }
-      qf[tt][ks] = as_f16x8(hv[0], hv[1], hv[2], hv[3]);
+      const uint32_t m = bf16x8_max_mag(qraw[tt][ks]);
+      mq = mq > m ? mq : m;
     }
+    const int kq = q_shift(group4_max_u32(mq));
+    sl2h[tt] = __builtin_ldexpf(a.scale_log2, -kq);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const u32x4 raw = qraw[tt][ks];
+      qf[tt][ks] = as_f16x8(bf16x2_pow2_to_f16x2(raw[0], kq), bf16x2_pow2_to_f16x2(raw[1], kq),
+                            bf16x2_pow2_to_f16x2(raw[2], kq), bf16x2_pow2_to_f16x2(raw[3], kq));
+    }
+  }
 
   float ref[HT], lsum[HT];  // softmax reference (base 2) and this lane's partial sum, per head 16tt+n
   f32x4 o[HT][32];          // O^T tile ct: O[head hw0+16tt+n][column 16ct+4g+i] = o[tt][ct][i]
@@ -431,11 +440,14 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = rbase + 16 * rt + 4 * g + i;
-          sv[rt][i] = row < n_valid ? sacc[rt][tt][i] * a.scale_log2 : -INFINITY;
+          // one rounding of the scaled score (no fused multiply-add into P below): the maximum, the
+          // reference and P all see the same value
+          sv[rt][i] = row < n_valid ? __fmul_rn(sacc[rt][tt][i], sl2h[tt]) : -INFINITY;
           m = fmaxf(m, sv[rt][i]);
         }
       m = group4_max(m);
-      const bool raise = m > ref[tt] + kWLazyRescale;
+      // a difference, not m > ref + 15: a large reference would absorb the 15 and let P overflow FP16
+      const bool raise = m - ref[tt] > kWLazyRescale;
       alpha[tt] = 1.0f;
       resc[tt] = false;
       if (__any(raise)) {  // the reference rises; O is rescaled in phase 2 (rare after the first step)
@@ -556,7 +568,9 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   if (tid == 0) sh.last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!sh.last) return;
-  // weights e^{lse_k - M} of every split, per head, in LDS (the ring is free): [wave][tt][head][split]
+  // weights e^{lse_k - M} of every split, per head, in LDS (the ring is free): [wave][tt][head][split].
+  // The splits are added in their order, this workgroup's own result rounded to FP16 as the stored ones
+  // are, so the merged bits do not depend on which split's workgroup merges.
   float* wts = reinterpret_cast<float*>(sh.ring);
   static_assert(kWWaves * 2 * 16 * 64 * 4 <= WGeo<FMT>::kSlots * WGeo<FMT>::kSlot, "merge weights fit the ring");
 #pragma unroll
@@ -577,17 +591,20 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
       Z += M == -INFINITY ? 0.0f : __expf(lk - M);
     }
     const float zinv = Z > 0.0f ? 1.0f / Z : 0.0f;
-    const float wown = M == -INFINITY ? 0.0f : __expf(lse[tt] - M) * inv[tt];
     u32x2* dst = reinterpret_cast<u32x2*>(a.out + hrow * kLatent + 4 * g);
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) {
-      f32x4 acc = o[tt][ct] * wown;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int k = 0; k < S; ++k) {
-        if (k == s || M == -INFINITY) continue;
+        if (M == -INFINITY) continue;
         const float wk = __expf(wh[k] - M);
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent + 4 * g);
-        const uint64_t x = __hip_atomic_load(const_cast<uint64_t*>(src + 4 * ct), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t x;
+        if (k == s) {
+          x = pack_h4(o[tt][ct] * inv[tt]);
+        } else {
+          const uint64_t* src = reinterpret_cast<const uint64_t*>(a.part_o + (hrow * S + k) * kLatent + 4 * g);
+          x = __hip_atomic_load(const_cast<uint64_t*>(src + 4 * ct), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         acc += wk * h4_to_f32x4(x);
       }
       acc *= zinv;
@@ -607,17 +624,10 @@ void launch_wide_one(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream) {
-  const bool dense = a.indices == nullptr;
-  if (a.H != 64 && a.H != 128) return hipErrorInvalidValue;
-  if (fmt == 0) {
-    if (dense) return hipErrorInvalidValue;
-    if (a.H == 64) launch_wide_one<1, 0, false>(a, stream);
-    else launch_wide_one<2, 0, false>(a, stream);
-  } else {
-    if (!dense) return hipErrorInvalidValue;
-    if (a.H == 64) launch_wide_one<1, 1, true>(a, stream);
-    else launch_wide_one<2, 1, true>(a, stream);
-  }
+  // NVFP4 rows and sparse lists only (uses_wide_kernel); other formats run the 32-head-group kernel
+  if (fmt != 0 || a.indices == nullptr || (a.H != 64 && a.H != 128)) return hipErrorInvalidValue;
+  if (a.H == 64) launch_wide_one<1, 0, false>(a, stream);
+  else launch_wide_one<2, 0, false>(a, stream);
   return hipGetLastError();
 }
 

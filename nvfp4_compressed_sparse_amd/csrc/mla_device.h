@@ -181,6 +181,56 @@ __device__ __forceinline__ float group4_sum(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Largest of the four values of lanes l, l^16, l^32, l^48 (unsigned), as group4_max.
+__device__ __forceinline__ uint32_t group4_max_u32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = r[0] > r[1] ? r[0] : r[1];
+  auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return q[0] > q[1] ? q[0] : q[1];
+}
+
+// ---- exact power-of-two normalisation of one head's query for FP16 matrix operands.
+// Every dequantized K / V value is exact in FP16, but FP16 spans only 2^-24 .. 65504 while a bf16 query
+// spans 2^-133 .. 3.4e38.  Each head's query is scaled by 2^k, with k chosen from the head's largest
+// magnitude so that this one lands in [2^15, 2^16): then no element overflows, every element within 2^29
+// of the largest converts exactly, and smaller ones round with an absolute error below 2^-25 of the
+// scaled largest, about 2^16 times below what the fp32 accumulation of the 576 products may already
+// lose.  The score is scaled back by 2^-k together with the softmax scale (exact: a power of two), so
+// a query and the same query times any power of two (with the softmax scale divided by it) give
+// bit-identical results.
+
+// Largest bf16 magnitude (bit pattern & 0x7FFF) among the 8 values of a 16-byte word.
+__device__ __forceinline__ uint32_t bf16x8_max_mag(u32x4 raw) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = raw[k] & 0x7FFFu, hi = (raw[k] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+// The shift k for a head whose largest magnitude has bf16 bits m (0: an all-zero head, k = 0).  For a
+// biased exponent e >= 1 the largest value lies in [2^(e-127), 2^(e-126)), so 2^(142-e) takes it to
+// [2^15, 2^16) (at most 65280 < 65504); a subnormal largest value (e = 0) is below 2^-126 and takes
+// k = 141.  k lies in [-112, 141].
+__device__ __forceinline__ int q_shift(uint32_t m) {
+  const int e = (int)(m >> 7);
+  return m == 0 ? 0 : 142 - (e > 0 ? e : 1);
+}
+
+// bf16 bits (16 bits of `bits` at position SHIFT*16) times 2^k, as FP16 (v_ldexp_f32: exact unless the
+// product leaves fp32's range, which |q| * 2^k < 2^16 rules out; then one rounding to FP16).
+__device__ __forceinline__ _Float16 bf16_pow2_to_f16(uint32_t bits16, int k) {
+  return (_Float16)__builtin_ldexpf(__uint_as_float(bits16 << 16), k);
+}
+
+// Two bf16 values of a dword (lo in .x) times 2^k, as FP16.
+__device__ __forceinline__ f16x2 bf16x2_pow2_to_f16x2(uint32_t d, int k) {
+  return f16x2{bf16_pow2_to_f16(d & 0xFFFFu, k), bf16_pow2_to_f16(d >> 16, k)};
+}
+
 // Workgroup barrier ordering LDS accesses only: this wave's LDS operations complete (lgkmcnt(0)),
 // then s_barrier.  Vector-memory loads still in flight (the next tiles' row gathers into other LDS
 // slots) are not waited for; the "memory" clobber keeps the compiler from moving memory accesses
@@ -245,11 +295,15 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t ra, uint32_t rb) {
 }
 
 // Agent-coherent relaxed accesses for the split results exchanged between workgroups.
-// Four floats as FP16 (round to nearest even) in one 8-byte agent-coherent store, and back to floats.
-__device__ __forceinline__ void store_coherent_h4(uint64_t* p, f32x4 v) {
+// Four floats as FP16 (round to nearest even) packed in 8 bytes, stored with one agent-coherent store, and
+// back to floats.  The merging workgroup rounds its own result the same way, so that a merge gives the
+// same bits whichever split's workgroup performs it.
+__device__ __forceinline__ uint64_t pack_h4(f32x4 v) {
   const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
-  const uint64_t x = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+}
+__device__ __forceinline__ void store_coherent_h4(uint64_t* p, f32x4 v) {
+  __hip_atomic_store(p, pack_h4(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ f32x4 h4_to_f32x4(uint64_t x) {
   const f16x2 lo = __builtin_bit_cast(f16x2, (uint32_t)x), hi = __builtin_bit_cast(f16x2, (uint32_t)(x >> 32));

@@ -11,6 +11,7 @@ namespace mla {
 // kTopkCtrlInts counters (both zero between calls), one segment (slot, count) per kTopkChunk positions,
 // and kTopkCap candidate (key, position) pairs.
 constexpr int kTopkChunk = 8192;
+constexpr int kTopkThreads = 512;  // workgroup size of the three top-k kernels
 constexpr int kTopkBits1 = 12;
 constexpr int kTopkCap = 8192;
 constexpr int kTopkCtrlInts = 8;

@@ -57,6 +57,18 @@ struct StageArgs {
   int32_t* staged_lens;       // [B*T]
 };
 
+constexpr int kDecodeThreads = 512;      // decode_kernel workgroup size
+constexpr int kWideDecodeThreads = 256;  // decode_wide_kernel workgroup size
+// A launch's grid, counted in threads, must fit 32 bits (the dispatch packet's grid size).
+constexpr int64_t kMaxLaunchThreads = 0xFFFFFFFFLL;
+// Split arrival counters live in a fixed region at the start of a split decode's workspace, one int32
+// per (query token, head group) up to this many.  No shape ever writes partial results there, and every
+// call leaves its counters at zero, so a zero-filled workspace stays valid for later calls of any shape.
+constexpr int64_t kMaxSplitCounters = 65536;
+
+// Tokens one writer call may take: the writers run one 64-lane wave per token.
+constexpr int64_t kMaxWriteTokens = kMaxLaunchThreads / 64;
+
 // Which decode kernel serves a shape: the wide-head kernel for NVFP4 rows with 64 or 128 heads (every
 // row dequantized once for all heads), the 16/32-head-group kernel otherwise.
 inline bool uses_wide_kernel(int fmt, int H) { return fmt == 0 && (H == 64 || H == 128); }

@@ -9,7 +9,8 @@
 // compute unit.  The split's list entries are resolved to slots (order kept) in LDS, and the heads'
 // latent q goes to LDS as f16; then, per step of 64 rows:
 //   * wave w scores rows 16w..16w+15 of the step for the 16 heads with MFMA 16x16x32: the latent part in
-//     f16 (q rounded to f16, the codes exact), the rope part in bf16 (both exact), one accumulator.  Lane
+//     f16 (each head's q scaled by a power of two into f16's range, then rounded to f16; the codes exact),
+//     the rope part in bf16 (both exact), one accumulator, the power of two undone in the score.  Lane
 //     l holds, for row l%16, the latent bytes 128(l/16)..+127 and rope dims 16(l/16)..+15, and in latent
 //     k-step ks feeds bytes 8ks..+7 of them (q's fragments use the same dimension order).  The scores
 //     (times the row's scale) and the scales go to LDS, then, past the step's first barrier, the latent
@@ -76,6 +77,7 @@ struct PthShared {
   _Float16 pp[16][72];            // P'[head][row] = p * row scale (f16), rows padded by 8
   float salpha[16];               // the step's rescale factor per head
   float sl[16], sm[16];           // the final l and m per head
+  int qk[16];                     // per head: q is scaled by 2^qk[h] (its largest magnitude to [2^15, 2^16))
 };
 
 // 4 E4M3 bytes -> f16x4 (exact)
@@ -102,11 +104,14 @@ __global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArg
 
   // the 16 heads' latent q, requested first so that it arrives during the list and page-table lookups:
   // thread tid takes head tid / 16, dims 32 (tid % 16) .. +31
+  // (and rope dims 512 + 4 (tid % 16) .. +3, for the head's largest magnitude)
   u32x4 qv[4];
+  u32x2 qrm;
   {
-    const uint16_t* qsrc = a.q + (id * a.H + 16 * hg + (tid >> 4)) * 576 + 32 * (tid & 15);
+    const uint16_t* qsrc = a.q + (id * a.H + 16 * hg + (tid >> 4)) * 576;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qsrc + 8 * j);
+    for (int j = 0; j < 4; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qsrc + 32 * (tid & 15) + 8 * j);
+    qrm = *reinterpret_cast<const u32x2*>(qsrc + 512 + 4 * (tid & 15));
   }
 
   // ---- this split's list entries -> slots, in list order
@@ -158,26 +163,52 @@ __global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArg
 #pragma unroll
   for (int k = 0; k < kPthEPT; ++k)
     if (vmask & (1u << k)) sh.slots[off++] = slot_k[k];
+  // the latent q to LDS as f16, each head scaled by its power of two 2^kq (largest magnitude over all 576
+  // dims to [2^15, 2^16)); the 16 threads of a head reduce its largest magnitude
+  uint32_t mq = bf16x8_max_mag(u32x4{qrm[0], qrm[1], 0u, 0u});
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {  // the latent q to LDS as f16
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t m = bf16x8_max_mag(qv[j]);
+    mq = mq > m ? mq : m;
+  }
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)mq, d, 16);
+    mq = mq > o ? mq : o;
+  }
+  const int kq = q_shift(mq);
+  if ((tid & 15) == 0) sh.qk[tid >> 4] = kq;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
     const u32x4 v = qv[j];
-    f16x8 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = (_Float16)bf16_to_f32(v[i] & 0xFFFFu);
-      f[2 * i + 1] = (_Float16)bf16_to_f32(v[i] >> 16);
-    }
-    *reinterpret_cast<f16x8*>(&sh.qs[tid >> 4][32 * (tid & 15) + 8 * j]) = f;
+    *reinterpret_cast<f16x8*>(&sh.qs[tid >> 4][32 * (tid & 15) + 8 * j]) =
+        as_f16x8(bf16x2_pow2_to_f16x2(v[0], kq), bf16x2_pow2_to_f16x2(v[1], kq), bf16x2_pow2_to_f16x2(v[2], kq),
+                 bf16x2_pow2_to_f16x2(v[3], kq));
   }
   __syncthreads();
 
   // ---- q fragments of head 16hg + r16: latent dims 128g + 8ks .. +7 from LDS in each step, rope dims
   // 16g + 8kr .. +7 in registers
+  // (the rope part times 2^kq of head r16 stays exact in bf16: it only moves the exponent, and the
+  // scaled values stay below 2^16; the score of head 4g+i is scaled back by 2^-kq with the softmax scale)
   const uint16_t* qh = a.q + (id * a.H + 16 * hg + r16) * 576;
   bf16x8 qr[2];
+  {
+    const int kr = sh.qk[r16];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    qr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + 512 + 16 * g + 8 * j));
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qh + 512 + 16 * g + 8 * j);
+      u32x4 sc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sc[i] = pack_hi16(__builtin_ldexpf(__uint_as_float(raw[i] << 16), kr),
+                          __builtin_ldexpf(__uint_as_float(raw[i] & 0xFFFF0000u), kr));
+      qr[j] = __builtin_bit_cast(bf16x8, sc);
+    }
+  }
+  float sl2h[4];  // softmax scale * log2(e) * 2^-kq of heads 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sl2h[i] = __builtin_ldexpf(a.scale_log2, -sh.qk[4 * g + i]);
 
   // softmax role: thread tid serves head sh_h = tid / 16 over rows 4 * (tid % 16) .. +3 of a step
   const int sh_h = tid >> 4, sh_r = 4 * (tid & 15);
@@ -223,7 +254,7 @@ __global__ __launch_bounds__(kPthThreads, 2) void pth_decode_kernel(PthDecodeArg
     acc = mfma16x16x32(qr[1], __builtin_bit_cast(bf16x8, sr.kr[1]), acc);
     const int row = 16 * w + r16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh.sz[row][4 * g + i] = sr.valid ? acc[i] * sr.sc * a.scale_log2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) sh.sz[row][4 * g + i] = sr.valid ? acc[i] * sr.sc * sl2h[i] : -INFINITY;
     // a row past the list gets scale 0 and stages zeros, so that whatever slot 0 holds (it is read in
     // its place) cannot reach O through 0 * NaN
     if (g == 0) sh.ss[row] = sr.valid ? sr.sc : 0.0f;

@@ -22,7 +22,7 @@
 
 namespace mla {
 
-constexpr int kTkThreads = 512;
+constexpr int kTkThreads = kTopkThreads;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkTile = 4 * kTkThreads;             // positions per load pass of a workgroup
 constexpr int kTkChunk = kTopkChunk;                // positions per workgroup

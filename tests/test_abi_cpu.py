@@ -80,6 +80,46 @@ def test_sparse_decode_argument_errors():
         assert _sparse(S=1) == 5
 
 
+def test_launch_size_limits():
+    """Grids past 2^32 - 1 threads, and split launches with more than 65,536 counters, are refused on the
+    host (sizes whose 32-bit grid product would wrap)."""
+    big = dict(ws=FAKE, wsb=1 << 62)
+    # 16 heads: B*T*S workgroups of 512 threads; 2^23 of them is 2^32 threads
+    assert _sparse(B=1 << 20, T=8, S=1) == 2
+    assert _sparse(B=(1 << 20) - 1, T=8, S=1, **big) in (5, 0)  # fits; reaches the device check
+    assert _sparse(B=1 << 16, T=2, S=64, **big) == 2
+    # split launches: at most 65,536 query tokens x head groups
+    assert _sparse(B=65537, T=1, S=2, **big) == 2
+    assert _sparse(B=65536, T=1, S=2, **big) in (5, 0)
+    # writers: one 64-lane wave per token, fewer than 2^26 tokens
+    assert _quant(n=1 << 26) == 2
+    assert _quant(n=(1 << 26) - 1) in (5, 0)
+    # top-k: n * ceil(ld / 8192) workgroups of 512 threads
+    assert _topk(n=1 << 23, ld=4096, wsb=1 << 62) == 2
+    assert _topk(n=(1 << 23) - 1, ld=4096, wsb=1 << 62) in (5, 0)
+    # stage: up to 16 workgroups of 256 threads per query token
+    assert _stage(B=1 << 20) == 2
+
+
+def test_sparse_fp8_decode_argument_errors():
+    def call(**kw):
+        a = dict(q=FAKE, pool=FAKE, ps=64 * 576, npg=10, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, B=2, T=1, H=16, k=256,
+                 sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=None, wsb=0, stream=None)
+        a.update(kw)
+        return M.lib().mla_sparse_decode_fp8(a["q"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"],
+                                             a["idx"], a["B"], a["T"], a["H"], a["k"], a["sc"], a["causal"], a["S"],
+                                             a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+    assert call(idx=None) == 1
+    assert call(ps=64 * 352) == 3  # an NVFP4-sized page is too small for 576-byte rows
+    assert call(k=2049) == 2
+    assert call(sc=3e38) == 2  # sm_scale * log2(e) overflows fp32
+    need = M.lib().mla_sparse_decode_fp8_workspace_bytes(2, 1, 16, 256, 2)
+    assert call(S=2, ws=FAKE, wsb=need - 1) == 4
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == 5
+
+
 def _dense(**kw):
     a = dict(q=FAKE, pool=FAKE, ps=64 * 576, npg=10, bt=FAKE, bts=4, ctx=FAKE, B=2, T=1, H=128, L=8192,
              sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30, stream=None)
@@ -134,12 +174,16 @@ def test_split_choice_and_workspace_sizes():
     assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 1) == 0
     rows = 64 * 32
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # a split counter per query token and 32-head group + FP16 partial outputs + fp32 partial lse
-    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 4) == (r256(64 * 4) + r256(rows * 4 * 512 * 2) +
-                                                                       r256(rows * 4 * 4))
-    assert L.mla_sparse_decode_workspace_bytes(8, 1, 128, 2048, 2) == (r256(8 * 4 * 4) +
-                                                                       r256(8 * 128 * 2 * 512 * 2) +
+    # the fixed region of 65,536 split counters (the same for every shape) + FP16 partial outputs + fp32
+    # partial lse
+    cnt = 65536 * 4
+    assert L.mla_sparse_decode_workspace_bytes(64, 1, 32, 2048, 4) == cnt + r256(rows * 4 * 512 * 2) + r256(rows * 4 * 4)
+    assert L.mla_sparse_decode_workspace_bytes(8, 1, 128, 2048, 2) == (cnt + r256(8 * 128 * 2 * 512 * 2) +
                                                                        r256(8 * 128 * 2 * 4))
+    assert L.mla_sparse_decode_fp8_workspace_bytes(64, 1, 32, 2048, 4) == L.mla_sparse_decode_workspace_bytes(
+        64, 1, 32, 2048, 4)
+    assert L.mla_sparse_decode_fp8_splits(64, 1, 32, 2048) == 4
+    assert L.mla_sparse_decode_fp8_splits(2, 1, 128, 2048) == 8  # 16/32-head groups at every H (4 x 2 units)
 
 
 def test_binding_rejects_cpu_tensors():
@@ -277,7 +321,12 @@ def test_pth_argument_errors():
         assert dec(**{name: None}) == 1, name
     assert dec(H=48) == 2 and dec(H=8) == 2 and dec(k=0) == 2 and dec(k=2049) == 2 and dec(S=65) == 2
     assert dec(scale=0.0) == 2 and dec(scale=float("inf")) == 2 and dec(causal=3) == 2 and dec(slots=63) == 2
-    assert dec(S=8, k=256) == 2  # more splits than 64-entry chunks
+    # a requested split count sets the chunk (rounded up to whole 64-entry steps): fewer splits may run,
+    # and the workspace query sizes for the same effective count
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 8) == r256(64 * 4 * 512 * 4) + r256(64 * 4 * 4)
+    assert M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 300, 4) == r256(64 * 3 * 512 * 4) + r256(64 * 3 * 4)
+    assert dec(S=8, k=256, wsb=M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 8) - 1) == 4
     assert dec(q=FAKE + 8) == 3 and dec(rope=FAKE + 8) == 3 and dec(out=FAKE + 2) == 3
     need = M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 2)
     assert need > 0 and M.lib().mla_sparse_decode_pth_workspace_bytes(2, 1, 32, 256, 1) == 0

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from cases import Case, bf16_to_np, compare_outputs
+from cases import Case, bf16_to_np, compare_outputs, v_abs_of_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -36,18 +36,18 @@ def gpu_pool(case, d):
     return d["pool"]
 
 
-def gpu_decode(case, d, num_splits=0, idx=None, q=None):
+def gpu_decode(case, d, num_splits=0, idx=None, q=None, sm_scale=None):
     c = case.cfg
     lse = torch.empty((c.B, c.T, c.H), dtype=torch.float32, device="cuda")
     qq = d["q"] if q is None else q
     if c.topk:
-        out, _ = M.mla_sparse_decode(qq, d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"],
-                                     d["idx"] if idx is None else idx, c.sm_scale, causal=c.causal,
-                                     num_splits=num_splits, lse=lse)
+        fn = M.mla_sparse_decode if c.fmt == "nvfp4" else M.mla_sparse_decode_fp8
+        out, _ = fn(qq, d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"], d["idx"] if idx is None else idx,
+                    c.sm_scale if sm_scale is None else sm_scale, causal=c.causal, num_splits=num_splits, lse=lse)
     else:
         out, _ = M.mla_dense_decode_fp8(qq, d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"],
-                                        int(case.lay.ctx.max()), c.sm_scale, causal=c.causal,
-                                        num_splits=num_splits, lse=lse)
+                                        int(case.lay.ctx.max()), c.sm_scale if sm_scale is None else sm_scale,
+                                        causal=c.causal, num_splits=num_splits, lse=lse)
     torch.cuda.synchronize()
     return bf16_to_np(out).reshape(c.B * c.T, c.H, 512), lse.cpu().numpy().astype(np.float64).reshape(c.B * c.T, c.H)
 
@@ -151,7 +151,7 @@ def test_sparse_decode_tiny_config():
     assert np.array_equal(d["pool"].cpu().numpy(), case.oracle_pool())
     out, lse = gpu_decode(case, d)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, "tiny"))
+    say(compare_outputs(out, ro, lse, rl, "tiny", vmax=case.vmax()))
 
 
 @pytest.mark.parametrize("H", [32, 128])
@@ -164,7 +164,7 @@ def test_sparse_decode_split_counts(S, H):
     gpu_pool(case, d)
     out, lse = gpu_decode(case, d, num_splits=S)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, f"S={S} H={H}"))
+    say(compare_outputs(out, ro, lse, rl, f"S={S} H={H}", vmax=case.vmax()))
 
 
 def _bf16_bits(x):
@@ -199,7 +199,7 @@ def test_softmax_reference_rises(H, pattern, S):
     gpu_pool(case, d)
     out, lse = gpu_decode(case, d, num_splits=S)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, f"{pattern} H={H} S={S}"))
+    say(compare_outputs(out, ro, lse, rl, f"{pattern} H={H} S={S}", vmax=case.vmax()))
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
@@ -211,7 +211,7 @@ def test_sparse_decode_heads_and_topk(H, topk):
     gpu_pool(case, d)
     out, lse = gpu_decode(case, d)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, f"H={H} topk={topk}"))
+    say(compare_outputs(out, ro, lse, rl, f"H={H} topk={topk}", vmax=case.vmax()))
 
 
 def test_sparse_decode_padding_and_invalid_entries():
@@ -236,7 +236,7 @@ def test_sparse_decode_padding_and_invalid_entries():
     for S in (1, 4):
         out, lse = gpu_decode(case, d, num_splits=S)
         ro, rl = case.oracle_decode()
-        say(compare_outputs(out, ro, lse, rl, f"invalid entries S={S}"))
+        say(compare_outputs(out, ro, lse, rl, f"invalid entries S={S}", vmax=case.vmax()))
         assert not out[3].any() and np.all(lse[3] == -np.inf)
 
 
@@ -253,7 +253,7 @@ def test_sparse_decode_causal_speculative_verify():
     for S in (0, 1, 2):
         out, lse = gpu_decode(case, d, num_splits=S)
         ro, rl = case.oracle_decode()
-        say(compare_outputs(out, ro, lse, rl, f"causal S={S}"))
+        say(compare_outputs(out, ro, lse, rl, f"causal S={S}", vmax=case.vmax()))
 
 
 def test_single_index_returns_that_row_exactly():
@@ -279,7 +279,7 @@ def test_zero_query_gives_mean_of_v():
     gpu_pool(case, d)
     out, lse = gpu_decode(case, d, num_splits=1)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, "q=0"))
+    say(compare_outputs(out, ro, lse, rl, "q=0", vmax=case.vmax()))
     # all heads see the same uniform weights
     assert np.array_equal(out[:, 0:1, :].repeat(16, 1), out)
 
@@ -293,8 +293,129 @@ def test_permuted_index_list_gives_same_result():
     perm = torch.from_numpy(case.idx[:, :, np.random.default_rng(1).permutation(512)].copy()).cuda()
     out1, lse1 = gpu_decode(case, d, num_splits=1, idx=perm)
     ro, rl = case.oracle_decode()
-    compare_outputs(out1, ro, lse1, rl, "permuted")
-    compare_outputs(out0, ro, lse0, rl, "original")
+    compare_outputs(out1, ro, lse1, rl, "permuted", vmax=case.vmax())
+    compare_outputs(out0, ro, lse0, rl, "original", vmax=case.vmax())
+
+
+# --------------------------------------------------------------------------- sparse decode over FP8 rows
+@pytest.mark.parametrize("H,topk,S", [(16, 2048, 0), (32, 300, 1), (32, 300, 3), (64, 77, 0), (128, 512, 2), (16, 1, 0)])
+def test_sparse_fp8_decode(H, topk, S):
+    """The FP8-cache arm of the pages' comparison: the same selection over 576-byte FP8 rows."""
+    case = Case(small(H=H, topk=topk, L=5000, fmt="fp8", seed=140 + H + topk))
+    say(f"sparse fp8 H={H} topk={topk} S={S}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    assert np.array_equal(d["pool"].cpu().numpy(), case.oracle_pool())
+    out, lse = gpu_decode(case, d, num_splits=S)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"sparse fp8 H={H} topk={topk} S={S}", vmax=case.vmax()))
+
+
+def test_sparse_fp8_decode_causal_padding_and_invalid_entries():
+    cfg = small(B=4, T=2, H=32, topk=400, L=2500, fmt="fp8", causal=True, seed=151)
+    case = Case(cfg, ctx=[2500, 900, 130, 2000])
+    idx = case.idx.copy()
+    idx[0, 0, :150] = -1
+    idx[1, 1, 10:30] = 10 ** 7
+    idx[2, 0, :] = -1  # empty selection
+    idx[3, 1, :5] = [1999, 1998, 1997, 1996, 1995]  # past token 1's causal limit (2000 - 2 + 1) except 1999
+    case.idx = idx
+    case.lay.block_table[0, 7] = case.lay.num_pages + 2  # positions on this page select nothing
+    say("sparse fp8 causal / padding / invalid")
+    d = case.to_device()
+    d["pool"].fill_(0xFF)  # unwritten rows read as NaN if they ever reached the output
+    gpu_pool(case, d)
+    for S in (1, 2, 0):
+        out, lse = gpu_decode(case, d, num_splits=S)
+        assert np.isfinite(out).all()
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(out, ro, lse, rl, f"sparse fp8 invalid entries S={S}", vmax=case.vmax()))
+        assert not out[4].any() and np.all(lse[4] == -np.inf)
+
+
+# --------------------------------------------------------------------------- the query's range
+def _q_times_pow2(qbits, k):
+    """bf16 bits of q * 2^k per element (k scalar or broadcastable); asserts the product is exact in bf16."""
+    x = W.bf16_to_f32(qbits).astype(np.float64) * np.exp2(np.asarray(k, np.float64))
+    bits = W.bf16_bits(x.astype(np.float32))
+    assert np.array_equal(W.bf16_to_f32(bits).astype(np.float64), x), "scaled query not exact in bf16"
+    return bits
+
+
+def _q_device(qbits):
+    return torch.from_numpy(qbits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt,H,topk", [("nvfp4", 16, 300), ("nvfp4", 32, 300), ("nvfp4", 64, 300),
+                                        ("nvfp4", 128, 300), ("fp8", 32, 300), ("fp8", 128, 0)])
+def test_query_times_power_of_two_gives_identical_results(fmt, H, topk):
+    """q * 2^k with sm_scale * 2^-k leaves every score unchanged.  Each head's query is normalised by a power
+    of two before its FP16 conversion, so the results are bit-identical for k far outside FP16's range
+    (|q| up to about 2^102 and down to about 2^-110), and they match the oracle."""
+    case = Case(small(B=2, H=H, topk=topk, L=1200, fmt=fmt, seed=160 + H))
+    d = case.to_device()
+    gpu_pool(case, d)
+    sm = case.cfg.sm_scale
+    for S in (1, 2):
+        base_out, base_lse = gpu_decode(case, d, num_splits=S)
+        ro, rl = case.oracle_decode()
+        say(compare_outputs(base_out, ro, base_lse, rl, f"{fmt} H={H} S={S} unscaled", vmax=case.vmax()))
+        for k in (-100, -30, 30, 100):
+            qk = _q_times_pow2(case.q, k)
+            out, lse = gpu_decode(case, d, num_splits=S, q=_q_device(qk), sm_scale=sm * 2.0 ** -k)
+            assert np.array_equal(out, base_out), f"k={k}: output differs from the unscaled query's"
+            assert np.array_equal(lse, base_lse), f"k={k}: lse differs from the unscaled query's"
+        say(f"{fmt} H={H} S={S}: bit-identical for q * 2^k, k = -100, -30, 30, 100")
+
+
+@pytest.mark.parametrize("fmt,H,topk", [("nvfp4", 16, 256), ("nvfp4", 32, 256), ("nvfp4", 128, 256),
+                                        ("fp8", 32, 256), ("fp8", 128, 0)])
+def test_query_outside_fp16_range_matches_oracle(fmt, H, topk):
+    """Finite bf16 queries outside FP16's range (elements up to 1e5 and 1e30, tiny ones down to 1e-38, bf16
+    subnormals included), each head on its own scale, with sm_scale set so that the scores are of order one:
+    the softmax weights then depend on every large element, and the outputs must match the oracle."""
+    cfg = small(B=2, H=H, topk=topk, L=1000, fmt=fmt, seed=170 + H)
+    case = Case(cfg)
+    rng = np.random.default_rng(171)
+    q = W.bf16_to_f32(case.q).astype(np.float64)
+    # heads in four groups: a 1e5-sized spike in each head among N(0,1) values; whole heads at 1e30; whole
+    # heads at 1e-30 with bf16 subnormals (~1e-39) mixed in; heads whose values span 1e-20 .. 1e20
+    g = np.arange(H) % 4
+    spike = rng.integers(0, 576, size=(cfg.B, cfg.T, H))
+    for b in range(cfg.B):
+        for h in np.nonzero(g == 0)[0]:
+            q[b, 0, h, spike[b, 0, h]] = 1.0e5 * np.sign(q[b, 0, h, spike[b, 0, h]] + 0.5)
+    q[:, :, g == 1, :] *= 1.0e30
+    q[:, :, g == 2, :] *= 1.0e-30
+    q[:, :, g == 2, ::7] *= 1.0e-9  # ~1e-39: bf16 subnormals
+    span = 10.0 ** rng.uniform(-20, 20, size=(cfg.B, cfg.T, int((g == 3).sum()), 576))
+    q[:, :, g == 3, :] *= span
+    qbits = W.bf16_bits(q.astype(np.float32))
+    assert np.isfinite(W.bf16_to_f32(qbits)).all()
+    assert (np.abs(W.bf16_to_f32(qbits)) > 65504).any() and ((qbits & 0x7F80) == 0).sum() > 100
+    # one sm_scale for all heads cannot make every head's scores of order one: run one head group at a
+    # time, each with its own scale, against the oracle with that scale
+    d = case.to_device()
+    gpu_pool(case, d)
+    case.q = qbits
+    dq = _q_device(qbits)
+    vm = case.vmax()
+    # scores of order one: the 1e5 spike times |K| ~ 1; 24 ~ sqrt(576) N(0,1) products for whole heads
+    for grp, sm in ((0, 1.0e-5), (1, 1.0 / 2.4e31), (2, 1.0 / 2.4e-29), (3, 1.0e-21)):
+        for S in (1, 2):
+            out, lse = gpu_decode(case, d, num_splits=S, q=dq, sm_scale=sm)
+            pool = case.oracle_pool()
+            if topk:
+                ro, rl, _ = oracle.sparse_decode(qbits, pool, cfg.page_stride, case.lay.num_pages, case.lay.block_table,
+                                                 case.lay.ctx, case.idx, sm, fmt=fmt)
+            else:
+                ro, rl, _ = oracle.dense_decode_fp8(qbits, pool, cfg.page_stride, case.lay.num_pages,
+                                                    case.lay.block_table, case.lay.ctx, sm)
+            sel = g == grp
+            # (the other groups' scores may leave fp32's range at this sm_scale: outside the contract)
+            assert np.isfinite(out[:, sel]).all() and np.isfinite(lse[:, sel]).all()
+            say(compare_outputs(out[:, sel], ro[:, sel], lse[:, sel], rl[:, sel], f"{fmt} H={H} group {grp} S={S}",
+                                vmax=vm))
 
 
 # --------------------------------------------------------------------------- dense FP8 decode
@@ -308,7 +429,7 @@ def test_dense_fp8_decode(T, causal, S):
     assert np.array_equal(d["pool"].cpu().numpy(), case.oracle_pool())
     out, lse = gpu_decode(case, d, num_splits=S)
     ro, rl = case.oracle_decode()
-    say(compare_outputs(out, ro, lse, rl, f"dense T={T} S={S}"))
+    say(compare_outputs(out, ro, lse, rl, f"dense T={T} S={S}", vmax=case.vmax()))
 
 
 def test_dense_fp8_pages_outside_the_pool():
@@ -327,7 +448,7 @@ def test_dense_fp8_pages_outside_the_pool():
     for S in (1, 3, 0):
         out, lse = gpu_decode(case, d, num_splits=S)
         ro, rl = case.oracle_decode()
-        say(compare_outputs(out, ro, lse, rl, f"dense invalid pages S={S}"))
+        say(compare_outputs(out, ro, lse, rl, f"dense invalid pages S={S}", vmax=case.vmax()))
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
@@ -348,7 +469,7 @@ def test_unwritten_pool_bytes_do_not_leak(fmt):
         out, lse = gpu_decode(case, d, num_splits=S)
         assert np.isfinite(out).all() and np.isfinite(lse).all()
         ro, rl = case.oracle_decode()
-        say(compare_outputs(out, ro, lse, rl, f"0xFF pool {fmt} S={S}"))
+        say(compare_outputs(out, ro, lse, rl, f"0xFF pool {fmt} S={S}", vmax=case.vmax()))
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
@@ -393,7 +514,7 @@ def test_block_major_multi_layer_pool(fmt):
                                                 lay.ctx, cfg.sm_scale)
         torch.cuda.synchronize()
         say(compare_outputs(bf16_to_np(out).reshape(cfg.B, H, 512), ro,
-                            lse.cpu().numpy().astype(np.float64).reshape(cfg.B, H), rl, f"layer {l}"))
+                            lse.cpu().numpy().astype(np.float64).reshape(cfg.B, H), rl, f"layer {l}", vmax=c.vmax()))
 
 
 # --------------------------------------------------------------------------- staged path (NVFP4 -> FP8 copy)
@@ -482,8 +603,12 @@ def test_staged_decode_matches_oracle(H):
     bt = (np.arange(nq)[:, None] * P + np.arange(P)[None, :]).astype(np.int32)
     ro, rl, _ = oracle.dense_decode_fp8(case.q.reshape(nq, 1, H, 576), ref_st.reshape(-1), 64 * 576, nq * P, bt, cnt,
                                         cfg.sm_scale)
+    vm = np.zeros((nq, 1, 512))
+    for u in range(nq):
+        if cnt[u]:
+            vm[u, 0] = v_abs_of_rows(ref_st[u, :cnt[u]], "fp8").max(0)
     say(compare_outputs(bf16_to_np(out).reshape(nq, H, 512), ro,
-                        lse.cpu().numpy().astype(np.float64).reshape(nq, H), rl, f"staged decode H={H}"))
+                        lse.cpu().numpy().astype(np.float64).reshape(nq, H), rl, f"staged decode H={H}", vmax=vm))
 
 
 # --------------------------------------------------------------------------- full-size configs, sampled
@@ -491,7 +616,7 @@ def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
     """Oracle results for sampled query tokens of a full-size device case: the selected source rows are
     copied to the host and quantized by the oracle into a small pool of their own."""
     lay = inp["layout"]
-    outs, lses, pools_ok = [], [], True
+    outs, lses, vmaxes, pools_ok = [], [], [], True
     idx_all = idx_d.cpu().numpy() if idx_d is not None else None
     q_all = q_d.view(torch.int16).cpu().numpy().view(np.uint16)
     for qt in qtoks:
@@ -517,7 +642,7 @@ def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
         q1 = q_all[b:b + 1]
         if idx_all is not None:
             o, l, _ = oracle.sparse_decode(q1, pool, cfg.page_stride, npg, mini_bt, ctx, idx_all[b:b + 1],
-                                           cfg.sm_scale, cfg.causal, units=[t])
+                                           cfg.sm_scale, cfg.causal, units=[t], fmt=cfg.fmt)
         else:
             o, l, _ = oracle.dense_decode_fp8(q1, pool, cfg.page_stride, npg, mini_bt, ctx, cfg.sm_scale, cfg.causal,
                                               units=[t])
@@ -532,10 +657,12 @@ def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
         oidx = (slots // 64) * cfg.page_stride + (slots % 64) * rb
         orows = pool[(oidx[:, None] + np.arange(rb)[None, :]).reshape(-1)].reshape(-1, rb)
         pools_ok &= np.array_equal(grows, orows)
-    return np.stack(outs), np.stack(lses), pools_ok
+        vmaxes.append(v_abs_of_rows(orows, cfg.fmt).max(0)[None, :] if orows.size else np.zeros((1, 512)))
+    return np.stack(outs), np.stack(lses), np.stack(vmaxes), pools_ok
 
 
-@pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b16", "pages15", "short35"])
+@pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b4", "dense_b8", "dense_b16", "pages15", "pages20",
+                                  "short35", "pages15_fp8"])
 def test_full_size_config_sampled(name):
     cfg = W.CONFIGS[name]
     say(f"full-size {name}: generating inputs")
@@ -552,21 +679,22 @@ def test_full_size_config_sampled(name):
     say(f"full-size {name}: decode")
     if cfg.topk:
         idx = inp["idx_sets"][0]
-        out, _ = M.mla_sparse_decode(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx,
-                                     cfg.sm_scale, causal=cfg.causal, lse=lse)
+        fn = M.mla_sparse_decode if cfg.fmt == "nvfp4" else M.mla_sparse_decode_fp8
+        out, _ = fn(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx, cfg.sm_scale,
+                    causal=cfg.causal, lse=lse)
     else:
         idx = None
         out, _ = M.mla_dense_decode_fp8(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"],
                                         int(lay.ctx.max()), cfg.sm_scale, causal=cfg.causal, lse=lse)
     torch.cuda.synchronize()
     nq = cfg.B * cfg.T
-    qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed).choice(nq, 6, replace=False))))
+    qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed).choice(nq, min(6, nq), replace=False))))
     say(f"full-size {name}: oracle on query tokens {qtoks}")
-    ro, rl, pools_ok = _sampled_oracle(cfg, inp, qtoks, idx, q)
+    ro, rl, vm, pools_ok = _sampled_oracle(cfg, inp, qtoks, idx, q)
     assert pools_ok, "pool rows differ from the oracle's quantization"
     g = bf16_to_np(out).reshape(nq, cfg.H, 512)[qtoks]
     gl = lse.cpu().numpy().astype(np.float64).reshape(nq, cfg.H)[qtoks]
-    say(compare_outputs(g, ro, gl, rl, f"full-size {name}"))
+    say(compare_outputs(g, ro, gl, rl, f"full-size {name}", vmax=vm))
     # the write chunk of the mixed step: bit exact on every row
     if cfg.quant_chunk:
         cl = inp["chunk_lat"].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -630,4 +758,5 @@ def test_full_size_staged_path_sampled():
         ro, rl, _ = oracle.dense_decode_fp8(q_h[b:b + 1, t:t + 1], ref[0].reshape(-1), 64 * 576, ref.shape[1] // 64,
                                             np.arange(ref.shape[1] // 64, dtype=np.int32)[None, :],
                                             np.array([n], np.int32), cfg.sm_scale)
-        say(compare_outputs(g_out[qt:qt + 1], ro, g_lse[qt:qt + 1], rl, f"staged token {qt}"))
+        vm = v_abs_of_rows(ref[0, :n], "fp8").max(0)[None, None, :]
+        say(compare_outputs(g_out[qt:qt + 1], ro, g_lse[qt:qt + 1], rl, f"staged token {qt}", vmax=vm))

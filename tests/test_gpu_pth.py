@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as W
-from cases import Case, bf16_to_np, compare_outputs
+from cases import Case, bf16_to_np, compare_outputs, selected_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,23 @@ def pth_buffers(case):
     return (lat_g, sc_g, rope_g), (lat_o, sc_o, rope_o)
 
 
+def pth_vmax(case, lat_o, sc_o, idx=None):
+    """Largest |V| = |code value * scale| per query token and column among its selected slots:
+    [B, T, 1, 512]."""
+    c = case.cfg
+    e4 = np.array([oracle.e4m3_value(x) for x in range(256)])
+    idx = case.idx if idx is None else idx
+    out = np.zeros((c.B, c.T, 1, 512))
+    num_pages = lat_o.shape[0] // 64
+    for b in range(c.B):
+        for t in range(c.T):
+            pos = selected_positions(case.lay.ctx, c.T, c.causal, idx, b, t, case.lay.block_table, num_pages)
+            if pos.size:
+                slots = case.lay.block_table[b, pos // 64].astype(np.int64) * 64 + pos % 64
+                out[b, t, 0] = np.abs(e4[lat_o[slots]] * sc_o[slots].astype(np.float64)[:, None]).max(0)
+    return out
+
+
 def small(B=2, T=1, H=16, topk=256, L=4096, causal=False, seed=7):
     return W.DecodeConfig("p", B=B, T=T, H=H, topk=topk, fmt="fp8", ctx=L, causal=causal, seed=seed)
 
@@ -75,18 +92,62 @@ def test_pth_write_bit_exact():
     assert np.array_equal(rope_g.view(torch.int16).cpu().numpy().view(np.uint16), rope_o)
 
 
-def run_case(case, num_splits=0, idx=None):
-    (lat_g, sc_g, rope_g), (lat_o, sc_o, rope_o) = pth_buffers(case)
+def run_case(case, num_splits=0, idx=None, q=None, sm_scale=None, buffers=None, raw=False):
+    (lat_g, sc_g, rope_g), (lat_o, sc_o, rope_o) = pth_buffers(case) if buffers is None else buffers
     c = case.cfg
     idx = case.idx if idx is None else idx
-    out, lse = M.mla_sparse_decode_pth(bf16_dev(case.q), lat_g, sc_g, rope_g, dev(case.lay.block_table),
-                                       dev(case.lay.ctx), dev(idx), c.sm_scale, causal=c.causal,
-                                       num_splits=num_splits)
+    q = case.q if q is None else q
+    sm = c.sm_scale if sm_scale is None else sm_scale
+    out, lse = M.mla_sparse_decode_pth(bf16_dev(q), lat_g, sc_g, rope_g, dev(case.lay.block_table),
+                                       dev(case.lay.ctx), dev(idx), sm, causal=c.causal, num_splits=num_splits)
     torch.cuda.synchronize()
-    ro, rl, _ = oracle.sparse_decode_pth(case.q, lat_o, sc_o, rope_o, case.lay.block_table, case.lay.ctx, idx,
-                                         c.sm_scale, c.causal)
     g = bf16_to_np(out)
-    return compare_outputs(g, ro, lse.cpu().numpy(), rl, "pth")
+    if raw:
+        return g, lse.cpu().numpy()
+    ro, rl, _ = oracle.sparse_decode_pth(q, lat_o, sc_o, rope_o, case.lay.block_table, case.lay.ctx, idx, sm,
+                                         c.causal)
+    return compare_outputs(g, ro, lse.cpu().numpy(), rl, "pth", vmax=pth_vmax(case, lat_o, sc_o, idx))
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_pth_query_times_power_of_two_gives_identical_results(H):
+    """As for the NVFP4 decode: q * 2^k with sm_scale * 2^-k, k far outside FP16's range, gives bit-identical
+    outputs (each head's query is normalised by a power of two), which match the oracle."""
+    case = Case(small(B=2, H=H, topk=300, L=1500, seed=97 + H))
+    bufs = pth_buffers(case)
+    say(run_case(case, num_splits=1, buffers=bufs))
+    for S in (1, 2):
+        base = run_case(case, num_splits=S, buffers=bufs, raw=True)
+        for k in (-100, -30, 30, 100):
+            x = W.bf16_to_f32(case.q).astype(np.float64) * 2.0 ** k
+            qk = W.bf16_bits(x.astype(np.float32))
+            assert np.array_equal(W.bf16_to_f32(qk).astype(np.float64), x)
+            got = run_case(case, num_splits=S, q=qk, sm_scale=case.cfg.sm_scale * 2.0 ** -k, buffers=bufs, raw=True)
+            assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1]), f"k={k} S={S}"
+
+
+def test_pth_query_outside_fp16_range_matches_oracle():
+    """A 1e5 spike among N(0,1) values and whole heads at 1e30 or 1e-30, with sm_scale setting the scores to
+    order one (one scale per run, checked on the heads it fits)."""
+    case = Case(small(B=2, H=16, topk=256, L=1200, seed=99))
+    bufs = pth_buffers(case)
+    rng = np.random.default_rng(98)
+    q = W.bf16_to_f32(case.q).astype(np.float64)
+    g = np.arange(16) % 3
+    for b in range(2):
+        for h in np.nonzero(g == 0)[0]:
+            q[b, 0, h, rng.integers(0, 512)] = 1.0e5
+    q[:, :, g == 1, :] *= 1.0e30
+    q[:, :, g == 2, :] *= 1.0e-30
+    qbits = W.bf16_bits(q.astype(np.float32))
+    for grp, sm in ((0, 1.0e-5), (1, 1.0 / 2.4e31), (2, 1.0 / 2.4e-29)):
+        out, lse = run_case(case, num_splits=0, q=qbits, sm_scale=sm, buffers=bufs, raw=True)
+        ro, rl, _ = oracle.sparse_decode_pth(qbits, bufs[1][0], bufs[1][1], bufs[1][2], case.lay.block_table,
+                                             case.lay.ctx, case.idx, sm)
+        sel = g == grp
+        assert np.isfinite(out[:, :, sel]).all()  # other groups' scores may leave fp32's range at this scale
+        say(compare_outputs(out[:, :, sel], ro[:, :, sel], lse[:, :, sel], rl[:, :, sel], f"pth group {grp}",
+                            vmax=pth_vmax(case, bufs[1][0], bufs[1][1])))
 
 
 @pytest.mark.parametrize("H", [16, 32, 128])
@@ -158,4 +219,6 @@ def test_pth_decode_full_size_sampled():
         idx1 = np.array([[[pos_of[int(p)] if p >= 0 else -1 for p in idx[b, 0]]]], np.int32)
         bt1 = np.arange(lat_o.shape[0] // 64, dtype=np.int32)[None, :]
         ro_, rl_, _ = oracle.sparse_decode_pth(q[b:b + 1], lat_o, sc_o, rope_o, bt1, [n], idx1, cfg.sm_scale)
-        say(compare_outputs(got[b:b + 1], ro_, lse_g[b:b + 1], rl_, f"pth full token {b}"))
+        e4 = np.array([oracle.e4m3_value(x) for x in range(256)])
+        vm = np.abs(e4[lat_o[:n]] * sc_o[:n].astype(np.float64)[:, None]).max(0)[None, None, None, :]
+        say(compare_outputs(got[b:b + 1], ro_, lse_g[b:b + 1], rl_, f"pth full token {b}", vmax=vm))

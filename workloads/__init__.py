@@ -83,6 +83,9 @@ CONFIGS = {
     "pages20": DecodeConfig("pages20", B=20, T=1, H=16, topk=2048, fmt="nvfp4", ctx=140000, seed=20260007),
     "short35": DecodeConfig("short35", B=35, T=1, H=16, topk=2048, fmt="nvfp4", ctx_range=(256, 2048),
                             seed=20260008),
+    # the third arm of the pages' comparison at the same shape and inputs as pages15 (same seed): the
+    # selected rows read from a 576-byte FP8 cache
+    "pages15_fp8": DecodeConfig("pages15_fp8", B=15, T=1, H=16, topk=2048, fmt="fp8", ctx=140000, seed=20260006),
 }
 
 
