@@ -159,6 +159,24 @@ int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes
                       size_t workspace_bytes, void* stream);
 
 /*
+ * mla_sparse_decode without a workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It runs the same
+ * kernels with the same split choice (same results, bit for bit) and allocates nothing: the split
+ * counters and partial results live in a 32 MiB device array inside the library, one per GPU the library
+ * runs on, held until the process ends (mla_noalloc_scratch_bytes() returns its size).  A call whose
+ * splits would need more than that (mla_sparse_decode_workspace_bytes(...) > mla_noalloc_scratch_bytes())
+ * returns MLA_ERR_WORKSPACE and enqueues nothing.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents; its split counters start at zero and every call returns them to zero.
+ * Calls that can overlap on one GPU (other streams, other threads) race on the array: serialize them.
+ * Arguments, other errors and results as for mla_sparse_decode.
+ */
+size_t mla_noalloc_scratch_bytes(void);
+int mla_sparse_decode_noalloc(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                              const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                              int32_t causal, int32_t num_splits, void* out, float* lse, void* stream);
+
+/*
  * Sparse MLA decode over 576-byte FP8 rows: the definition of mla_sparse_decode with K = the E4M3 values
  * of the row (analysis page, row table: 512 latent + 64 rope bytes, no per-row scale), over a pool
  * written by mla_kv_quant_fp8 (page_stride_bytes >= 64*576).  This is the third arm of the launch post's

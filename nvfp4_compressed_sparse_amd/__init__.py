@@ -24,7 +24,7 @@ EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
     "mla_sparse_decode", "mla_sparse_decode_fp8_splits", "mla_sparse_decode_fp8_workspace_bytes",
-    "mla_sparse_decode_fp8", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
+    "mla_sparse_decode_fp8", "mla_noalloc_scratch_bytes", "mla_sparse_decode_noalloc", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
     "mla_sparse_decode_pth_workspace_bytes", "mla_sparse_decode_pth", "mla_index_key_quant", "mla_index_logits",
     "mla_index_topk_workspace_bytes", "mla_index_topk",
 ]
@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
         "mla_sparse_decode_fp8_splits": (ctypes.c_int, [i32, i32, i32, i32]),
+        "mla_noalloc_scratch_bytes": (sz, []),
+        "mla_sparse_decode_noalloc": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P,
+                                                     P, P]),
         "mla_sparse_decode_fp8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "mla_sparse_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P, P,
                                                  P, sz, P]),
@@ -226,6 +229,28 @@ def mla_sparse_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, co
     return _sparse("mla_sparse_decode_fp8", "mla_sparse_decode_fp8_workspace_bytes", q, pool, page_stride_bytes,
                    num_pages, block_table, context_lens, indices, sm_scale, causal, num_splits, out, lse, workspace,
                    stream)
+
+
+def mla_sparse_decode_noalloc(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,
+                              causal=False, num_splits=0, out=None, lse=None, stream=None):
+    """mla_sparse_decode with the library's own scratch array instead of a workspace (the call allocates
+    nothing; out and lse must then be given): returns (out, lse)."""
+    import torch
+    _common(q, pool, block_table, context_lens)
+    _dev(indices, torch.int32, "indices")
+    B, T, H, _ = q.shape
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, T) or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [B, T, topk] int32 tensor")
+    if out is None:
+        raise ValueError("out must be given (the call allocates nothing)")
+    out, lse, _ = _decode_io(q, out, lse, None, 0)
+    st = lib().mla_sparse_decode_noalloc(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+                                         block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(),
+                                         indices.data_ptr(), B, T, H, indices.shape[2], float(sm_scale),
+                                         int(bool(causal)), int(num_splits), out.data_ptr(),
+                                         None if lse is None else lse.data_ptr(), _stream(stream))
+    _check("mla_sparse_decode_noalloc", st)
+    return out, lse
 
 
 def mla_sparse_decode_fp8_splits(B, T, H, topk):

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "mla_internal.h"
 #include "mla_nvfp4.h"
@@ -196,6 +197,38 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
 
 }  // namespace
 
+// ---- scratch of the entry point that allocates nothing (mla_sparse_decode_noalloc).  The split arrival
+// counters and partial results live in this file-scope device array instead of a caller workspace: the
+// fixed counter region first (zero at module load; every call returns the counters it used to zero, and
+// no call writes anything else there), then the partials.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address is looked up once per device with hipGetSymbolAddress
+// and only that address is handed to kernels.
+namespace {
+
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLA_OK;
+}
+
+}  // namespace
+
 int mla::check_device_status() { return check_device(); }
 
 extern "C" {
@@ -295,6 +328,31 @@ int mla_sparse_decode_fp8(const void* q, const void* pool, int64_t page_stride_b
   int S = num_splits ? num_splits : mla_sparse_decode_fp8_splits(B, T, H, topk);
   return run_decode(1, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
                     topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t mla_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+int mla_sparse_decode_noalloc(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                              const int32_t* indices, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                              int32_t causal, int32_t num_splits, void* out, float* lse, void* stream) {
+  int st = check_decode_common(q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, B, T, H,
+                               sm_scale, causal, out, MLA_NVFP4_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (!indices) return MLA_ERR_NULL;
+  if (!aligned(indices, 4)) return MLA_ERR_STRIDE_ALIGN;
+  if (topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_SHAPE;
+  const int S = num_splits ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
+  const size_t need = workspace_for(B, T, H, S);
+  if (need > kNoallocScratchBytes) return MLA_ERR_WORKSPACE;  // more partial results than the scratch holds
+  void* ws = nullptr;
+  if (need > 0) {
+    if ((st = check_device()) != MLA_OK) return st;
+    if ((st = scratch_address(&ws)) != MLA_OK) return st;
+  }
+  return run_decode(0, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
+                    topk, sm_scale, causal, S, out, lse, ws, need, stream);
 }
 
 int mla_dense_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,

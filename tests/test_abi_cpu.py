@@ -120,6 +120,28 @@ def test_sparse_fp8_decode_argument_errors():
         assert call() == 5
 
 
+def test_noalloc_decode_argument_errors():
+    L = M.lib()
+    cap = L.mla_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+
+    def call(**kw):
+        a = dict(q=FAKE, pool=FAKE, ps=64 * 352, npg=10, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, B=2, T=1, H=16, k=256,
+                 sc=0.07, causal=0, S=0, out=FAKE, lse=None, stream=None)
+        a.update(kw)
+        return L.mla_sparse_decode_noalloc(a["q"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"], a["idx"],
+                                           a["B"], a["T"], a["H"], a["k"], a["sc"], a["causal"], a["S"], a["out"],
+                                           a["lse"], a["stream"])
+    assert call(idx=None) == 1 and call(q=None) == 1
+    assert call(H=48) == 2 and call(k=0) == 2 and call(S=65) == 2
+    # splits whose partial results exceed the scratch array: refused before any device call
+    assert L.mla_sparse_decode_workspace_bytes(256, 1, 32, 2048, 64) > cap
+    assert call(B=256, H=32, k=2048, S=64) == 4
+    import torch
+    if not torch.cuda.is_available():
+        assert call(S=4) == 5  # fits: reaches the device check
+
+
 def _dense(**kw):
     a = dict(q=FAKE, pool=FAKE, ps=64 * 576, npg=10, bt=FAKE, bts=4, ctx=FAKE, B=2, T=1, H=128, L=8192,
              sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30, stream=None)
