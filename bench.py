@@ -109,6 +109,10 @@ def main():
                          "to an FP8 copy, then the FP8 decoder reads it), or the per-token-head FP8 layout "
                          "(FP8 latent, fp32 scale, bf16 rope in three buffers) and its decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-rate probes (streaming read, row gather, MFMA loop) run after the timing")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step's calls as captured HIP graphs instead of prepared launches")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
@@ -229,41 +233,81 @@ def main():
         S = args.splits or 0
         pth_ws = M.lib().mla_sparse_decode_pth_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.topk, S)
 
-    def step(i, ev=None):
-        k = i % N_SETS
+    def write(i):
+        """The step's quantize-on-write (the same new rows every step), on the current stream."""
+        st = torch.cuda.current_stream()
         if pth_path:
-            M.mla_kv_quant_pth(w_lat, w_rope, w_slots, pth_lat, pth_sc, pth_rope, stream=stream)
-            if ev is not None:
-                ev[0].record(stream)
+            M.mla_kv_quant_pth(w_lat, w_rope, w_slots, pth_lat, pth_sc, pth_rope, stream=st)
+        else:
+            quant(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=st)
+
+    def decode(i):
+        """The step's decode call over index set i % N_SETS, on the current stream."""
+        k = i % N_SETS
+        st = torch.cuda.current_stream()
+        if pth_path:
             M.mla_sparse_decode_pth(q_sets[k], pth_lat, pth_sc, pth_rope, inp["bt"], inp["ctx"], idx_sets[k],
-                                    cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-            return
-        quant(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        if staged_path:
+                                    cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, stream=st)
+        elif staged_path:
             M.mla_stage_nvfp4_fp8(pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k],
                                   causal=cfg.causal, staged=staged, staged_block_table=st_bt, staged_lens=st_len,
-                                  stream=stream)
+                                  stream=st)
             M.mla_dense_decode_fp8(q_sets[k].view(nq, 1, cfg.H, 576), staged, 64 * 576, nq * st_pages, st_bt, st_len,
                                    st_pages * 64, cfg.sm_scale, num_splits=S, out=out1, lse=lse1, workspace=ws,
-                                   stream=stream)
+                                   stream=st)
         elif cfg.topk:
             sparse_fn(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k], cfg.sm_scale,
-                      causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=stream)
+                      causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=st)
         else:
             M.mla_dense_decode_fp8(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], max_ctx,
                                    cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
-                                   stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+                                   stream=st)
 
     for i in range(args.warmup):
-        step(i)
+        write(i)
+        decode(i)
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps), splits={S}")
+    if args.graph:
+        # The step's calls captured once as HIP graphs (the write, and the decode of each index set) and replayed.
+        # Nothing in a captured call allocates or clears memory (the split counters return to zero inside the
+        # decode kernel).  Measured slower than the prepared launches below on this software stack.
+        g_write = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_write):
+            write(0)
+        g_dec = []
+        for k in range(N_SETS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                decode(k)
+            g_dec.append(g)
+        torch.cuda.synchronize()
+        for i in range(max(args.warmup, N_SETS)):
+            g_write.replay()
+            g_dec[i % N_SETS].replay()
+        torch.cuda.synchronize()
+
+        def step(i, ev):
+            g_write.replay()
+            ev[0].record(stream)
+            g_dec[i % N_SETS].replay()
+            ev[1].record(stream)
+    else:
+        # The step's calls with their arguments checked and converted once (the binding's prepared calls): each
+        # step then costs the host two plain C-ABI calls, so the host stays ahead of the GPU and the timed loop
+        # measures the GPU rather than the host's launch path.
+        w_call = M.prepare(write, 0)
+        d_calls = [M.prepare(decode, k) for k in range(N_SETS)]
+
+        def step(i, ev):
+            w_call()
+            ev[0].record(stream)
+            d_calls[i % N_SETS]()
+            ev[1].record(stream)
+
+        for i in range(N_SETS):
+            step(i, (torch.cuda.Event(), torch.cuda.Event()))
+        torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps), splits={S}, {'graph replay' if args.graph else 'prepared launches'}")
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -319,6 +363,17 @@ def main():
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)
 
+    if not args.no_peaks:
+        peaks = measure_achievable(cfg, pool if not pth_path else None, inp, idx_sets if cfg.topk else None, lay, lim_d
+                                   if cfg.topk else None)
+        roof["achievable"] = peaks
+        if roof["bound"] == "hbm":
+            roof["frac_of_stream_read"] = round(roof["achieved"] / peaks["stream_read_GBs"], 4)
+            if peaks.get("row_gather_GBs"):
+                roof["frac_of_row_gather"] = round(roof["achieved"] / peaks["row_gather_GBs"], 4)
+        else:
+            roof["frac_of_mfma_loop"] = round(roof["achieved"] / peaks["mfma_f16_TFLOPs"], 4)
+
     res = {
         "metric": "NVFP4 sparse-MLA decode query-tokens/s at B=64, top-2048; % of roofline",
         "value": round(value, 1),
@@ -338,13 +393,77 @@ def main():
                    "row_bytes_read": 644 if pth_path else cfg.row_bytes,
                    "index_padding": "position 0" if args.pad_as_row0 else "-1 (skipped)",
                    "step": ("quantize %d rows + %s" % (cfg.quant_chunk or nq,
-                                                       "stage + FP8 decode" if staged_path else "decode"))},
+                                                       "stage + FP8 decode" if staged_path else "decode")),
+                   "launch": ("hip graph replay (write graph + decode graph per step)" if args.graph else
+                              "prepared C-ABI calls (arguments checked once), write + decode per step")},
         "roofline": roof,
         "cpu_baseline": None,
     }
     if cpu is not None:
         res["cpu_baseline"] = run_cpu_baseline(cfg, cpu)
     print(json.dumps(res), flush=True)
+
+
+def measure_achievable(cfg, pool, inp, idx_sets, lay, lim_d):
+    """Rates this GPU reaches, measured here with the probe kernels (libmla_probe.so), each timed with HIP
+    events: a streaming read of a 4 GiB buffer, a gather of the step's selected rows from the pool (the decode's
+    access pattern: the valid rows of each index set, rotating over the sets), and a loop of independent FP16 and
+    bf16 MFMAs."""
+    import torch
+    from nvfp4_compressed_sparse_amd import probe
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3  # seconds
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    wg = 256 * 8
+    sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+    probe.stream_read(buf, sink, wg, sh)
+    t = timed(lambda i: probe.stream_read(buf, sink, wg, sh), 10)
+    out["stream_read_GBs"] = round(nbytes / t / 1e9, 1)
+    out["stream_read_bytes"] = nbytes
+    del buf
+    torch.cuda.empty_cache()
+    if pool is not None and idx_sets:
+        addrs = []
+        for ix in idx_sets:
+            b = torch.arange(cfg.B, device="cuda").view(cfg.B, 1, 1).expand_as(ix)
+            ok = (ix >= 0) & (ix <= lim_d)
+            pos = ix[ok].long()
+            bb = b[ok]
+            page = inp["bt"][bb, torch.clamp(pos >> 6, max=inp["bt"].shape[1] - 1)].long()
+            keep = (page >= 0) & (page < lay.num_pages) & ((pos >> 6) < inp["bt"].shape[1])
+            a16 = (page[keep] * cfg.page_stride + (pos[keep] & 63) * cfg.row_bytes) // 16
+            addrs.append(a16.to(torch.int32).contiguous())
+        chunks = cfg.row_bytes // 16
+        n = max(a.numel() for a in addrs)
+        gwg = (n * chunks + 256 * 6 - 1) // (256 * 6)
+        gsink = torch.empty(gwg * 256, dtype=torch.int32, device="cuda")
+        for a in addrs:
+            probe.row_gather(pool, a, cfg.row_bytes, gsink, gwg, sh)
+        t = timed(lambda i: probe.row_gather(pool, addrs[i % len(addrs)], cfg.row_bytes, gsink, gwg, sh), 24)
+        rows = float(np.mean([a.numel() for a in addrs]))
+        out["row_gather_GBs"] = round(rows * cfg.row_bytes / t / 1e9, 1)
+        out["row_gather_us"] = round(t * 1e6, 2)
+        out["row_gather_rows"] = int(rows)
+    iters, mwg = 2000, 256 * 8
+    mout = torch.empty(mwg * 256 * 4, dtype=torch.float32, device="cuda")
+    for bf16, key in ((0, "mfma_f16_TFLOPs"), (1, "mfma_bf16_TFLOPs")):
+        probe.mfma(bf16, iters, mout, mwg, sh)
+        t = timed(lambda i: probe.mfma(bf16, iters, mout, mwg, sh), 5)
+        out[key] = round(probe.mfma_flops(iters, mwg) / t / 1e12, 1)
+    log(f"[bench] achievable: {out}")
+    return out
 
 
 def bench_index_topk(args):

@@ -86,6 +86,44 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+# While `prepare` runs a binding function, its C-ABI calls are recorded instead of made.
+_recording = None
+
+
+def _call(name, *args):
+    if _recording is not None:
+        _recording.append((getattr(lib(), name), name, args))
+        return 0
+    return getattr(lib(), name)(*args)
+
+
+class Prepared:
+    """C-ABI call(s) of one binding call with their arguments checked and converted once (see prepare)."""
+
+    def __init__(self, calls, keep):
+        self._calls = calls
+        self._keep = keep  # the tensors whose addresses the calls hold
+
+    def __call__(self):
+        for fn, name, args in self._calls:
+            st = fn(*args)
+            if st != 0:
+                raise MlaError(name, st)
+
+
+def prepare(fn, *args, **kwargs):
+    """Check and convert the arguments of a binding call once, e.g. prepare(mla_sparse_decode, q, ...,
+    out=out, workspace=ws, stream=s); the returned callable enqueues the same C-ABI call(s) again on the same
+    stream, with no per-call validation.  Its tensors must stay alive, in place and of the same shape."""
+    global _recording
+    _recording = []
+    try:
+        result = fn(*args, **kwargs)
+    finally:
+        calls, _recording = _recording, None
+    return Prepared(calls, (args, kwargs, result))
+
+
 def _check(fn, status):
     if status != 0:
         raise MlaError(fn, status)
@@ -128,7 +166,7 @@ def _quant(fn_name, k_nope, k_rope, slot_mapping, pool, page_stride_bytes, num_p
     # the last page's 64 rows must lie inside the pool (which may be one layer of a block-major cache)
     if num_pages < 1 or pool.numel() < page_stride_bytes * (num_pages - 1) + PAGE_TOKENS * row_bytes:
         raise ValueError("pool too small for num_pages pages of page_stride_bytes")
-    st = getattr(lib(), fn_name)(k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+    st = _call(fn_name, k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
                                  slot_mapping.data_ptr(), n, pool.data_ptr(), int(page_stride_bytes), int(num_pages),
                                  _stream(stream))
     _check(fn_name, st)
@@ -206,7 +244,7 @@ def _sparse(fn, ws_fn, q, pool, page_stride_bytes, num_pages, block_table, conte
     topk = indices.shape[2]
     ws = getattr(lib(), ws_fn)(B, T, H, topk, int(num_splits))
     out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
-    st = getattr(lib(), fn)(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+    st = _call(fn, q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
                             block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), indices.data_ptr(),
                             B, T, H, topk, float(sm_scale), int(bool(causal)), int(num_splits), out.data_ptr(),
                             None if lse is None else lse.data_ptr(), None if workspace is None else workspace.data_ptr(),
@@ -244,7 +282,7 @@ def mla_sparse_decode_noalloc(q, pool, page_stride_bytes, num_pages, block_table
     if out is None:
         raise ValueError("out must be given (the call allocates nothing)")
     out, lse, _ = _decode_io(q, out, lse, None, 0)
-    st = lib().mla_sparse_decode_noalloc(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+    st = _call("mla_sparse_decode_noalloc", q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
                                          block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(),
                                          indices.data_ptr(), B, T, H, indices.shape[2], float(sm_scale),
                                          int(bool(causal)), int(num_splits), out.data_ptr(),
@@ -268,7 +306,7 @@ def mla_dense_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, con
     B, T, H, _ = q.shape
     ws = lib().mla_dense_decode_workspace_bytes(B, T, H, int(max_context), int(num_splits))
     out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
-    st = lib().mla_dense_decode_fp8(q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+    st = _call("mla_dense_decode_fp8", q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
                                     block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), B, T, H,
                                     int(max_context), float(sm_scale), int(bool(causal)), int(num_splits),
                                     out.data_ptr(), None if lse is None else lse.data_ptr(),
@@ -304,7 +342,7 @@ def mla_stage_nvfp4_fp8(pool, page_stride_bytes, num_pages, block_table, context
     if staged.numel() < B * T * P * PAGE_TOKENS * FP8_ROW_BYTES or tuple(staged_block_table.shape) != (B * T, P) \
             or staged_lens.numel() != B * T:
         raise ValueError("staged buffers have the wrong size")
-    st = lib().mla_stage_nvfp4_fp8(pool.data_ptr(), int(page_stride_bytes), int(num_pages), block_table.data_ptr(),
+    st = _call("mla_stage_nvfp4_fp8", pool.data_ptr(), int(page_stride_bytes), int(num_pages), block_table.data_ptr(),
                                    block_table.stride(0), context_lens.data_ptr(), indices.data_ptr(), B, T, topk,
                                    int(bool(causal)), staged.data_ptr(), staged_block_table.data_ptr(),
                                    staged_lens.data_ptr(), _stream(stream))
@@ -333,7 +371,7 @@ def mla_kv_quant_pth(k_nope, k_rope, slot_mapping, lat, scale, rope, stream=None
     if (lat.shape != (slots, LATENT_DIM) or rope.shape != (slots, ROPE_DIM) or not lat.is_contiguous()
             or not rope.is_contiguous() or not scale.is_contiguous() or not slot_mapping.is_contiguous()):
         raise ValueError("lat [slots, 512], scale [slots] and rope [slots, 64] must be contiguous")
-    st = lib().mla_kv_quant_pth(k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+    st = _call("mla_kv_quant_pth", k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0),
                                 slot_mapping.data_ptr(), n, lat.data_ptr(), scale.data_ptr(), rope.data_ptr(), slots,
                                 _stream(stream))
     _check("mla_kv_quant_pth", st)
@@ -362,7 +400,7 @@ def mla_sparse_decode_pth(q, lat, scale, rope, block_table, context_lens, indice
         out = torch.empty((B, T, H, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
-    st = lib().mla_sparse_decode_pth(q.data_ptr(), lat.data_ptr(), scale.data_ptr(), rope.data_ptr(), scale.numel(),
+    st = _call("mla_sparse_decode_pth", q.data_ptr(), lat.data_ptr(), scale.data_ptr(), rope.data_ptr(), scale.numel(),
                                      block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
                                      indices.data_ptr(), B, T, H, topk, float(sm_scale), int(bool(causal)),
                                      int(num_splits), out.data_ptr(), lse.data_ptr(),
@@ -390,7 +428,7 @@ def mla_index_key_quant(keys, slot_mapping, pool, page_stride_bytes, num_pages, 
         raise ValueError("slot_mapping and pool must be contiguous")
     if num_pages < 1 or pool.numel() < page_stride_bytes * (num_pages - 1) + INDEX_PAGE_BYTES:
         raise ValueError("pool too small for num_pages pages of page_stride_bytes")
-    st = lib().mla_index_key_quant(keys.data_ptr(), keys.stride(0), slot_mapping.data_ptr(), n, pool.data_ptr(),
+    st = _call("mla_index_key_quant", keys.data_ptr(), keys.stride(0), slot_mapping.data_ptr(), n, pool.data_ptr(),
                                    int(page_stride_bytes), int(num_pages), _stream(stream))
     _check("mla_index_key_quant", st)
 
@@ -421,7 +459,7 @@ def mla_index_logits(q, w, pool, page_stride_bytes, num_pages, block_table, cont
     _dev(out, torch.float32, "out")
     if out.dim() != 2 or out.shape[0] != B * T or out.shape[1] < max_context or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B*T, >= max_context] tensor")
-    st = lib().mla_index_logits(q.data_ptr(), w.data_ptr(), HI, pool.data_ptr(), int(page_stride_bytes),
+    st = _call("mla_index_logits", q.data_ptr(), w.data_ptr(), HI, pool.data_ptr(), int(page_stride_bytes),
                                 int(num_pages), block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
                                 B, T, int(max_context), int(bool(causal)), out.data_ptr(), out.shape[1],
                                 _stream(stream))
@@ -460,7 +498,7 @@ def mla_index_topk(logits, lengths, k, out=None, workspace=None, stream=None):
     if workspace is None:
         workspace = torch.zeros(ws, dtype=torch.uint8, device=logits.device)  # counters start at zero
     _dev(workspace, torch.uint8, "workspace")
-    st = lib().mla_index_topk(logits.data_ptr(), ld, lengths.data_ptr(), n, int(k), out.data_ptr(),
+    st = _call("mla_index_topk", logits.data_ptr(), ld, lengths.data_ptr(), n, int(k), out.data_ptr(),
                               workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check("mla_index_topk", st)
     return out

@@ -11,6 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_nvfp4.so")
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")  # measurement probes for the benchmark (not the decode path)
 SOURCES = ["mla_quant.hip", "mla_decode.hip", "mla_decode_wide.hip", "mla_stage.hip", "mla_topk.hip", "mla_indexer.hip",
            "mla_pth.hip", "mla_abi.hip", "mla_abi_index.hip", "mla_abi_pth.hip"]
 
@@ -30,7 +31,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library (always rebuilds)."""
+    """Compile every HIP source for gfx950 and link the shared libraries (always rebuilds): the decode
+    library and the measurement probes."""
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -45,14 +47,15 @@ def build(verbose: bool = False) -> str:
             print(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], capture_output=True,
-                       text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(compile_one, SOURCES + ["mla_probe.hip"]))
+    for lib, parts in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        r = subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *parts, "-o", tmp], capture_output=True,
+                           text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -28,7 +28,8 @@
 //     block scale).  It then forms P = 2^(s - ref) (base-2 scores) with the current softmax reference
 //     and writes it to LDS as FP16.
 //   * lazy, speculative softmax reference: ref (per head) is shared by all waves and changes only when
-//     a score exceeds it by more than 2^8 (so P stays below 256).  A score wave that sees such a score
+//     a score exceeds it by more than 15 in base 2 (so P stays below 2^15, inside FP16's range; a rise
+//     costs a second barrier and rewrites of P and O, so it should be rare).  A score wave that sees such a score
 //     raises a flag and publishes its per-head maxima; after the barrier every wave reads the flag and,
 //     in that rare case, all of them derive the new reference from the published maxima, the
 //     accumulators are rescaled and the score waves rewrite P before one extra barrier.
@@ -49,7 +50,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kStepRows = 64;
 constexpr int kMaxChunk = 2048;        // list entries one workgroup holds
 constexpr int kEntriesPerThread = kMaxChunk / kThreads;
-constexpr float kLazyRescale = 8.0f;   // log2 headroom of the lazy softmax reference
+constexpr float kLazyRescale = 15.0f;  // log2 headroom of the lazy softmax reference (P < 2^15 in FP16)
 constexpr int kPStride = kStepRows * 2 + 16;  // bytes per head of a P tile: 64 FP16 values + padding
 constexpr int kTileStride = kLatent + 4;       // floats per head of a split's result tile in LDS (padded)
 constexpr int kPrologueSteps = 3;              // steps gathered before step 0 is awaited
@@ -104,6 +105,7 @@ struct Shared {
   int wcount[kWaves];
   int last;                         // this workgroup merges the splits
   float tile_lse[NH];               // lse of this workgroup's split, per head
+  int qshift[NH];                   // each head's query is scaled by 2^qshift[h] (q_shift of its largest |q|)
 };
 
 // The new reference of every head after a raise, from the score waves' maxima of the step (identical
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int lim = a.causal ? L - a.T + t : L - 1;
   if (tid < 2) sh.flag[tid] = 0;
   // published maxima start at -inf: a raise takes the largest published value, and only waves that
-  // raise publish (every score a wave saw before stays within 2^8 of the reference it left behind)
+  // raise publish (every score a wave saw before stays within 2^15 of the reference it left behind)
   if (tid < 2 * NH * 4) (&sh.smax[0][0][0])[tid] = -INFINITY;
   int n_valid;
   if constexpr (DENSE) {
@@ -379,31 +381,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // when nearly all of them have; the staggered issue lets the first steps' requests queue first.
     // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
     issue_upto(kEarly - 1);
+    lds_barrier();  // the FP16 query tile and the heads' shifts are in LDS (matches the accumulate waves' barrier)
     // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
-    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17); the four lane groups together hold
-    // the head's 576 values.  Each head is scaled by its power of two 2^kq (largest magnitude to
-    // [2^15, 2^16)), and its score scale by 2^-kq.
+    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17), read from the tile the accumulate waves
+    // converted (each head scaled by its power of two 2^kq); the head's score scale is scaled by 2^-kq.
     f16x8 qf[HT][18];
     float sl2h[HT];  // softmax scale * log2(e) * 2^-kq of head 16tt+n
 #pragma unroll
     for (int tt = 0; tt < HT; ++tt) {
-      auto qword = [&](int ks) {
+      sl2h[tt] = __builtin_ldexpf(a.scale_log2, -sh.qshift[16 * tt + n]);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
         const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-        return *reinterpret_cast<const u32x4*>(qstage + 2 * ((16 * tt + n) * kQK + d));
-      };
-      uint32_t mq = 0;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint32_t m = bf16x8_max_mag(qword(ks));
-        mq = mq > m ? mq : m;
-      }
-      const int kq = q_shift(group4_max_u32(mq));
-      sl2h[tt] = __builtin_ldexpf(a.scale_log2, -kq);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const u32x4 raw = qword(ks);
-        qf[tt][ks] = as_f16x8(bf16x2_pow2_to_f16x2(raw[0], kq), bf16x2_pow2_to_f16x2(raw[1], kq),
-                              bf16x2_pow2_to_f16x2(raw[2], kq), bf16x2_pow2_to_f16x2(raw[3], kq));
+        qf[tt][ks] = *reinterpret_cast<const f16x8*>(qstage + 2 * ((16 * tt + n) * kQK + d));
       }
     }
     issue_upto(kFirst - 1);
@@ -464,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         // scores of rows 16rt+4g+i, heads 16tt+n; base-2 maxima; speculative P = 2^(scale*s - ref) with
         // the current ref.  Only the last step can hold rows past the list (its padding): masked -inf.
         // The scaled score is rounded once (no fused multiply-add) and both the maxima and P use that
-        // rounded value, and the reference test compares a difference: so P <= 2^8 holds exactly even
+        // rounded value, and the reference test compares a difference: so P <= 2^15 holds exactly even
         // where scores are large enough for an added 8 to round away.
         const int rbase = k * kStepRows + 16 * rt + 4 * g;
         // (dense: a step whose page is not in the pool selects nothing)
@@ -540,6 +530,44 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
+  {
+    // The query tile converted to FP16 in place, each head scaled by its power-of-two shift (from the
+    // largest magnitude of its 576 values), here while the score waves issue their first gathers: the 256
+    // lanes of the four accumulate waves split the heads, 256 / NH lanes per head, each lane taking every
+    // (256/NH)-th 16-byte word of the head's 72 (it reads, then rewrites, only its own words).
+    constexpr int LPH = 256 / NH;                          // lanes per head: 8 or 16
+    constexpr int CPL = (kQK / 8 + LPH - 1) / LPH;         // words per lane: 9, or 5 (the last partial)
+    const int la = (w - 4) * 64 + lane;
+    const int hq = la / LPH, part = la % LPH;
+    uint8_t* qh = qstage + 2 * hq * kQK;
+    u32x4 qc[CPL];
+    uint32_t mq = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = part + LPH * i;
+      if (c < kQK / 8) {
+        qc[i] = *reinterpret_cast<const u32x4*>(qh + 16 * c);
+        const uint32_t m = bf16x8_max_mag(qc[i]);
+        mq = mq > m ? mq : m;
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < LPH; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)mq, d, 64);
+      mq = mq > o ? mq : o;
+    }
+    const int kq = q_shift(mq);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = part + LPH * i;
+      if (c < kQK / 8)
+        *reinterpret_cast<f16x8*>(qh + 16 * c) =
+            as_f16x8(bf16x2_pow2_to_f16x2(qc[i][0], kq), bf16x2_pow2_to_f16x2(qc[i][1], kq),
+                     bf16x2_pow2_to_f16x2(qc[i][2], kq), bf16x2_pow2_to_f16x2(qc[i][3], kq));
+    }
+    if (part == 0) sh.qshift[hq] = kq;
+  }
+  lds_barrier();  // the FP16 query tile and the shifts are in LDS (matches the score waves' barrier)
   lds_barrier();  // step 0 visible; the score waves hold their query fragments
   const int cq = r4;
   f32x4 o[HT][8];  // O^T tile c: O[head 16t+n][column 128cq+32g+8i+c] = o[t][c][i]

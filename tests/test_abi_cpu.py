@@ -11,8 +11,8 @@ import nvfp4_compressed_sparse_amd as M
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    with open(os.path.join(ROOT, "include", "mla_nvfp4.h")) as f:
+def _declared_functions(header="mla_nvfp4.h"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
@@ -25,6 +25,17 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(M.EXPORTS)
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from nvfp4_compressed_sparse_amd import probe
+    names = _declared_functions("mla_probe.h")
+    assert set(names) == set(probe.EXPORTS)
+    for n in names:
+        assert hasattr(probe.lib(), n), n
+    assert probe.lib().mla_probe_stream_read(None, 1 << 20, FAKE, 1, None) == 1  # bad argument: nothing launched
+    assert probe.lib().mla_probe_row_gather(FAKE, FAKE, 1000, 352, FAKE, 1, None) == 2  # grid too small
+    assert probe.mfma_flops(10, 2) == 2 * 4 * 10 * 8 * 16 * 16 * 32 * 2
 
 
 def test_version_and_status_strings():
