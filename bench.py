@@ -286,11 +286,12 @@ def main():
             g_dec[i % N_SETS].replay()
         torch.cuda.synchronize()
 
-        def step(i, ev):
+        def step(i):
             g_write.replay()
-            ev[0].record(stream)
             g_dec[i % N_SETS].replay()
-            ev[1].record(stream)
+
+        def dec_call(i):
+            g_dec[i % N_SETS].replay()
     else:
         # The step's calls with their arguments checked and converted once (the binding's prepared calls): each
         # step then costs the host two plain C-ABI calls, so the host stays ahead of the GPU and the timed loop
@@ -298,34 +299,42 @@ def main():
         w_call = M.prepare(write, 0)
         d_calls = [M.prepare(decode, k) for k in range(N_SETS)]
 
-        def step(i, ev):
+        def step(i):
             w_call()
-            ev[0].record(stream)
             d_calls[i % N_SETS]()
-            ev[1].record(stream)
+
+        def dec_call(i):
+            d_calls[i % N_SETS]()
 
         for i in range(N_SETS):
-            step(i, (torch.cuda.Event(), torch.cuda.Event()))
+            step(i)
         torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps), splits={S}, {'graph replay' if args.graph else 'prepared launches'}")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # The timed steps: HIP events on the launch stream at the two ends only.  An event recorded between the
+    # calls of a step puts a marker between the kernels, which costs several microseconds per step here.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
-    dec_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    dec_avg_us = float(np.mean(dec_us))
+    # The decode call's average duration: the same decode calls back to back, events at the two ends.
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for i in range(args.steps):
+        dec_call(i)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_avg_us = d0.elapsed_time(d1) * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (events), wall {wall / args.steps * 1e6:.2f} "
-        f"us/step; decode call avg {dec_avg_us:.2f} us, p10 {np.percentile(dec_us, 10):.2f}, "
-        f"p90 {np.percentile(dec_us, 90):.2f}")
+        f"us/step; decode call avg {dec_avg_us:.2f} us over {args.steps} back-to-back calls")
 
     nq = cfg.B * cfg.T
     value = nq / (ms_per_step * 1e-3)
@@ -350,15 +359,15 @@ def main():
         roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent")
     if staged_path:
         roof["kernel"] = ("mla_stage_nvfp4_fp8 + mla_dense_decode_fp8 calls: stage_rows_kernel then decode_kernel "
-                          "over the FP8 copy, timed together with HIP events on their stream")
+                          "over the FP8 copy, back-to-back calls timed together with HIP events on their stream")
     elif pth_path:
-        roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), timed "
-                          "with HIP events on their stream")
+        roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), "
+                          "back-to-back calls timed with HIP events on their stream")
     else:
         roof["kernel"] = (("mla_sparse_decode_fp8" if sparse_fp8 else "mla_sparse_decode") if cfg.topk
                           else "mla_dense_decode_fp8") + " call: " + \
             ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
-            " (split merge inside), timed with HIP events on its stream"
+            " (split merge inside), back-to-back calls timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)
@@ -406,7 +415,7 @@ def main():
 
 def measure_achievable(cfg, pool, inp, idx_sets, lay, lim_d):
     """Rates this GPU reaches, measured here with the probe kernels (libmla_probe.so), each timed with HIP
-    events: a streaming read of a 4 GiB buffer, a gather of the step's selected rows from the pool (the decode's
+    events over back-to-back calls: a streaming read of a 4 GiB buffer, a gather of the step's selected rows from the pool (the decode's
     access pattern: the valid rows of each index set, rotating over the sets), and a loop of independent FP16 and
     bf16 MFMAs."""
     import torch
@@ -415,13 +424,15 @@ def measure_achievable(cfg, pool, inp, idx_sets, lay, lim_d):
     sh = stream.cuda_stream
 
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i in range(reps):
-            evs[i][0].record(stream)
-            fn(i)
-            evs[i][1].record(stream)
+        # back-to-back calls, events at the two ends only (as the decode call is timed): seconds per call
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3  # seconds
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
 
     out = {}
     nbytes = 4 << 30
@@ -493,12 +504,8 @@ def bench_index_topk(args):
     log(f"[bench] index top-k: {n} rows, ld={ld}, k={cfg.topk}, {N_SETS} logit sets of "
         f"{n * ld * 4 / 1e6:.1f} MB")
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(i):
         M.mla_index_topk(sets[i % N_SETS], lens_d, cfg.topk, out=out, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -506,19 +513,17 @@ def bench_index_topk(args):
     chosen = int((out >= 0).sum().item())
     if chosen != int(np.minimum(lengths, cfg.topk).sum()):
         raise SystemExit(f"index top-k chose {chosen} positions, expected {int(np.minimum(lengths, cfg.topk).sum())}")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # a step is one call: back-to-back calls, HIP events on their stream at the two ends only
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    call_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    call_avg = float(np.mean(call_us))
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step; call avg {call_avg:.2f} us, "
-        f"p10 {np.percentile(call_us, 10):.2f}, p90 {np.percentile(call_us, 90):.2f}")
+    call_avg = ms_per_step * 1e3
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (one call each)")
     # algorithmic bytes: every logit of every row read once, the lists written
     bytes_per = int(lengths.astype(np.int64).sum() * 4 + n * cfg.topk * 4)
     ach = bytes_per / (call_avg * 1e-6) / 1e9
@@ -598,30 +603,24 @@ def bench_index_logits(args):
     out = torch.empty((n, (maxc + 3) // 4 * 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(i):
         M.mla_index_logits(q_sets[i % N_SETS], w_sets[i % N_SETS], pool, ps, lay.num_pages, bt, ctx, maxc,
                            causal=cfg.causal, out=out, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # a step is one call: back-to-back calls, HIP events on their stream at the two ends only
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    call_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    call_avg = float(np.mean(call_us))
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step; call avg {call_avg:.2f} us, "
-        f"p10 {np.percentile(call_us, 10):.2f}, p90 {np.percentile(call_us, 90):.2f}")
+    call_avg = ms_per_step * 1e3
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (one call each)")
     # algorithmic work: each request's keys (128 code bytes + a 4-byte scale per position) read once, the
     # query tokens' q and w read, one fp32 logit written per (query token, visible position)
     visible = sum(W.position_limit(int(lay.ctx[b]), cfg.T, t, cfg.causal) + 1
@@ -749,17 +748,22 @@ def bench_dsa_step(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed steps with events at the two ends only; then the same steps with an event between stages (the
+    # markers add a few microseconds each) for the per-stage split
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     stage = [float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])) for j in range(3)]
-    log(f"[bench] dsa step: {ms_per_step * 1e3:.1f} us/step; logits {stage[0]:.1f}, top-k {stage[1]:.1f}, "
-        f"write + decode {stage[2]:.1f} us")
+    log(f"[bench] dsa step: {ms_per_step * 1e3:.1f} us/step; with stage markers: logits {stage[0]:.1f}, "
+        f"top-k {stage[1]:.1f}, write + decode {stage[2]:.1f} us")
     res = {
         "metric": "sparse decode step (indexer logits + top-k + NVFP4 sparse-MLA decode) query-tokens/s",
         "value": round(n / (ms_per_step * 1e-3), 1),
