@@ -467,7 +467,7 @@ def measure_achievable(cfg, pool, inp, idx_sets, lay, lim_d):
         out["row_gather_GBs"] = round(rows * cfg.row_bytes / t / 1e9, 1)
         out["row_gather_us"] = round(t * 1e6, 2)
         out["row_gather_rows"] = int(rows)
-    iters, mwg = 2000, 256 * 8
+    iters, mwg = 4000, 256 * 16
     mout = torch.empty(mwg * 256 * 4, dtype=torch.float32, device="cuda")
     for bf16, key in ((0, "mfma_f16_TFLOPs"), (1, "mfma_bf16_TFLOPs")):
         probe.mfma(bf16, iters, mout, mwg, sh)

@@ -239,18 +239,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // staged page-table entries visible
 
+  // a position past the limit, or on a page beyond the table width (only with a context longer than
+  // the table allows), selects nothing; every table read of the lane is issued before any is used
+  // (LDS reads from the staged table; a table too wide to stage is read from memory)
+  bool inr[EPT];
+  int pgc[EPT], page[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int pg = (pos[k] >= 0 ? pos[k] : 0) >> 6;
+    inr[k] = pos[k] >= 0 && pos[k] <= lim && pg < npg;
+    pgc[k] = inr[k] ? pg : 0;
+  }
+  if (staged) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) page[k] = btl[pgc[k]];
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) page[k] = inr[k] ? btg[pgc[k]] : -1;
+  }
   uint32_t addr[EPT];
   uint32_t vmask = 0;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    const int pg = (pos[k] >= 0 ? pos[k] : 0) >> 6;
-    // a position past the limit, or on a page beyond the table width (only with a context longer than
-    // the table allows), selects nothing
-    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg < npg;
-    int page = -1;
-    if (inr) page = staged ? btl[pg] : btg[pg];
-    const bool ok = inr && page >= 0 && page < a.num_pages;
-    addr[k] = ok ? (uint32_t)(((uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(pos[k] & 63) * ROWB) >> 4) : 0u;
+    const bool ok = inr[k] && page[k] >= 0 && page[k] < a.num_pages;
+    addr[k] = ok ? (uint32_t)(((uint64_t)page[k] * (uint64_t)a.page_stride + (uint64_t)(pos[k] & 63) * ROWB) >> 4)
+                 : 0u;
     vmask |= (uint32_t)ok << k;
   }
   // order-keeping compaction (entries ordered by thread, then k): this lane's offset in the wave is
@@ -296,6 +309,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     g_off[u] = c < G::kChunks ? 16u * c : 0u;
     if (DENSE) g_off[u] += (uint32_t)((G::kWaveRows * r4 + g_row[u]) * ROWB);
   }
+  // sparse: the 16-byte row addresses of this wave's loads of step st, from the LDS row list; rows past
+  // the list (last step only) read its first row (their scores are masked)
+  auto step_addrs = [&](int st, uint32_t (&a16)[NL]) {
+    const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
+    if ((st + 1) * kStepRows <= n_valid) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
+    } else {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int r = st * kStepRows + G::kWaveRows * r4 + g_row[u];
+        a16[u] = sh.rowlist[r < n_valid ? r : 0];
+      }
+    }
+  };
+  // sparse: load u of this wave's share of step st (row chunks read once: streaming loads)
+  auto issue_load = [&](int st, int u, uint32_t a16) {
+    const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
+    const uint8_t* src = a.pool + ((uint64_t)a16 * 16u + g_off[u]);
+    if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16<true>(src, dst + 1024 * u);
+  };
   auto issue_step = [&](int st) {  // the gathering role only
     const uint8_t* dst = slot_ptr(st) + G::kWaveRows * r4 * RS;
     if constexpr (DENSE) {
@@ -319,25 +353,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     } else {
-      const uint32_t* rl = sh.rowlist + st * kStepRows + G::kWaveRows * r4;
-      // every row address is read first (one LDS round trip), then the loads go out; rows past the list
-      // (last step only) read its first row (their scores are masked)
+      // every row address is read first (one LDS round trip), then the loads go out
       uint32_t a16[NL];
-      if ((st + 1) * kStepRows <= n_valid) {
+      step_addrs(st, a16);
 #pragma unroll
-        for (int u = 0; u < NL; ++u) a16[u] = rl[g_row[u]];
-      } else {
-#pragma unroll
-        for (int u = 0; u < NL; ++u) {
-          const int r = st * kStepRows + G::kWaveRows * r4 + g_row[u];
-          a16[u] = sh.rowlist[r < n_valid ? r : 0];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const uint8_t* src = a.pool + ((uint64_t)a16[u] * 16u + g_off[u]);
-        if (u < NL - 1 || 64 * u + lane < G::kWaveChunks) dma16(src, dst + 1024 * u);
-      }
+      for (int u = 0; u < NL; ++u) issue_load(st, u, a16[u]);
     }
   };
   // The score waves gather.  Issuing a step's LDS-DMA loads stalls the issuing wave for a while (the

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
       // chunk offset folded into the 16-byte row address before the 64-bit add: no per-lane 64-bit
       // pointers stay live across the loop
       const uint8_t* src = a.pool + (uint64_t)(a16[u] + (uint32_t)(c < G::kChunks ? c : 0)) * 16u;
-      if (u < NL - 1 || e < G::kWaveChunks) dma16(src, dst + 1024 * u);
+      if (u < NL - 1 || e < G::kWaveChunks) dma16<true>(src, dst + 1024 * u);
     }
   };
 

@@ -252,17 +252,31 @@ __device__ __forceinline__ int xcd_logical_id(int hw, int n) {
 // LDS-DMA of 16 bytes per lane: lane l's global bytes land at lds + 16*l (lds must be wave-uniform).
 // Issued through asm so that the compiler's waitcnt tracking does not drain the gathers still in
 // flight; completion is awaited explicitly with vmcnt.  M0 is saved and restored around the load.
+// STREAM marks data read once (the cache rows): a non-temporal load, so that the stream does not push
+// the data that is reused (queries, tables, split results, the kernel's code) out of the L2.
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(m)
-      : "memory");
+  if constexpr (STREAM) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m)
+        : "memory");
+  }
 }
 
 template <int N>

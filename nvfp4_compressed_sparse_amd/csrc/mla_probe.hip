@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "mla_probe.h"
 
 namespace {
@@ -16,7 +17,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 
 constexpr int kThreads = 256;
 
@@ -64,39 +64,55 @@ __global__ __launch_bounds__(kThreads) void row_gather_kernel(const uint8_t* __r
 }
 
 // Each wave runs `iters` rounds of kChains independent MFMAs (enough to keep the matrix pipeline full) on
-// register operands, then writes its accumulators (so that none of the work can be dropped).
+// register operands, then writes its accumulators (so that none of the work can be dropped).  The round is
+// written in assembly: compiled from builtins, the compiler moved the accumulators between register files
+// inside the loop, and those moves, not the matrix pipeline, set the rate.
 constexpr int kChains = 8;
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float* __restrict__ out) {
-  f32x4 acc[kChains];
-#pragma unroll
-  for (int c = 0; c < kChains; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const float s = 1.0f + 1e-3f * (float)(threadIdx.x & 7);
-  if constexpr (BF16) {
-    bf16x8 a, b;
+  f16x8 a, b;  // FP16 bit patterns; read as bf16 by the bf16 instruction (any finite values will do)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      a[e] = (__bf16)(s * (float)e);
-      b[e] = (__bf16)(s - 0.01f * (float)e);
-    }
-    for (int it = 0; it < iters; ++it)
-#pragma unroll
-      for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-  } else {
-    f16x8 a, b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      a[e] = (_Float16)(s * (float)e);
-      b[e] = (_Float16)(s - 0.01f * (float)e);
-    }
-    for (int it = 0; it < iters; ++it)
-#pragma unroll
-      for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (_Float16)(s * (float)e);
+    b[e] = (_Float16)(s - 0.01f * (float)e);
   }
-  f32x4 t = acc[0];
+  f32x4 c[kChains];
 #pragma unroll
-  for (int c = 1; c < kChains; ++c) t += acc[c];
+  for (int k = 0; k < kChains; ++k) c[k] = f32x4{s * k, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (BF16) {
+      asm volatile(
+          "v_mfma_f32_16x16x32_bf16 %0, %8, %9, %0\n\t"
+          "v_mfma_f32_16x16x32_bf16 %1, %8, %9, %1\n\t"
+          "v_mfma_f32_16x16x32_bf16 %2, %8, %9, %2\n\t"
+          "v_mfma_f32_16x16x32_bf16 %3, %8, %9, %3\n\t"
+          "v_mfma_f32_16x16x32_bf16 %4, %8, %9, %4\n\t"
+          "v_mfma_f32_16x16x32_bf16 %5, %8, %9, %5\n\t"
+          "v_mfma_f32_16x16x32_bf16 %6, %8, %9, %6\n\t"
+          "v_mfma_f32_16x16x32_bf16 %7, %8, %9, %7"
+          : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7])
+          : "v"(a), "v"(b));
+    } else {
+      asm volatile(
+          "v_mfma_f32_16x16x32_f16 %0, %8, %9, %0\n\t"
+          "v_mfma_f32_16x16x32_f16 %1, %8, %9, %1\n\t"
+          "v_mfma_f32_16x16x32_f16 %2, %8, %9, %2\n\t"
+          "v_mfma_f32_16x16x32_f16 %3, %8, %9, %3\n\t"
+          "v_mfma_f32_16x16x32_f16 %4, %8, %9, %4\n\t"
+          "v_mfma_f32_16x16x32_f16 %5, %8, %9, %5\n\t"
+          "v_mfma_f32_16x16x32_f16 %6, %8, %9, %6\n\t"
+          "v_mfma_f32_16x16x32_f16 %7, %8, %9, %7"
+          : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7])
+          : "v"(a), "v"(b));
+    }
+  }
+  // the hazard between an MFMA writing a register and a VALU reading it is left to the wait below
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  f32x4 t = c[0];
+#pragma unroll
+  for (int k = 1; k < kChains; ++k) t += c[k];
   reinterpret_cast<f32x4*>(out)[(int64_t)blockIdx.x * kThreads + threadIdx.x] = t;
 }
 
