@@ -285,18 +285,24 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((uint16_t)((N & 15) | ((N >> 4) << 14) | 0x0F70));
 }
 
-// Wait until at most k steps of this wave's gathers (NL loads each) are still in flight, 0 <= k <= 5
-// (larger k waits as for 5).
+// Wait until at most k steps of this wave's gathers (NL loads each) are still in flight, 0 <= k <= 7
+// (larger k waits as for 7; a count the 6-bit vmcnt cannot hold waits for as many steps as it can).
+template <int NL, int K>
+__device__ __forceinline__ void wait_steps_le() {
+  constexpr int kMaxSteps = 63 / NL;
+  wait_vmem_le<(K < kMaxSteps ? K : kMaxSteps) * NL>();
+}
 template <int NL>
 __device__ __forceinline__ void wait_steps(int k) {
-  static_assert(5 * NL < 64, "vmcnt range");
-  switch (k) {
-    case 0: wait_vmem_le<0>(); break;
-    case 1: wait_vmem_le<NL>(); break;
-    case 2: wait_vmem_le<2 * NL>(); break;
-    case 3: wait_vmem_le<3 * NL>(); break;
-    case 4: wait_vmem_le<4 * NL>(); break;
-    default: wait_vmem_le<5 * NL>(); break;
+  switch (k <= 0 ? 0 : k) {
+    case 0: wait_steps_le<NL, 0>(); break;
+    case 1: wait_steps_le<NL, 1>(); break;
+    case 2: wait_steps_le<NL, 2>(); break;
+    case 3: wait_steps_le<NL, 3>(); break;
+    case 4: wait_steps_le<NL, 4>(); break;
+    case 5: wait_steps_le<NL, 5>(); break;
+    case 6: wait_steps_le<NL, 6>(); break;
+    default: wait_steps_le<NL, 7>(); break;
   }
 }
 
