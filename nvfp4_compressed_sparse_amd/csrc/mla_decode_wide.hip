@@ -1,5 +1,6 @@
-// MLA decode for 64 or 128 heads over a paged cache of NVFP4 (352-byte) or FP8 (576-byte) rows, for
-// gfx950: every selected row is gathered and dequantized once for all heads of its query token.
+// MLA decode for 64 or 128 heads over a paged cache of NVFP4 (352-byte) rows with sparse lists, for
+// gfx950: every selected row is gathered and dequantized once for all heads of its query token.  (FP8
+// rows and dense decodes at these head counts run the 32-head-group kernel.)
 //
 // What it computes is the same as the 16/32-head kernel (launch post, section "原生 NVFP4 稀疏 MLA 解码
 // 内核" (native NVFP4 sparse MLA decode kernel); the analysis page, section "A kernel that reads four
@@ -41,9 +42,8 @@ constexpr float kWRefMargin = 4.0f;              // a risen reference sits this 
 constexpr int kKStride = kQK * 2 + 16;           // bytes per row of the FP16 K tile (bank spread)
 constexpr int kVStride = kWStep * 2 + 16;        // bytes per column of the FP16 V^T tile (bank spread)
 
-template <int FMT>
 struct WGeo {
-  static constexpr int kRowBytes = FMT == 0 ? kNvfp4Row : kFp8Row;
+  static constexpr int kRowBytes = kNvfp4Row;
   static constexpr int kChunks = kRowBytes / 16;                 // 22 or 36 per row
   static constexpr int kStride = kRowBytes + 16;                 // LDS bytes per raw row
   static constexpr int kWaveRows = kWStep / kWWaves;             // 8 rows per wave per step
@@ -52,12 +52,11 @@ struct WGeo {
   static_assert((kLoads - 1) * 64 < kWaveChunks, "only a wave's last gather load is partial");
   static_assert(8 * 64 * 16 <= kWaveRows * kKStride, "rescale staging fits a wave's rows of the K tile");
   static constexpr int kSlot = kWStep * kStride;
-  static constexpr int kSlots = FMT == 0 ? 6 : 3;                // ring depth
+  static constexpr int kSlots = 6;                               // ring depth
 };
 
-template <int FMT>
 struct WShared {
-  uint8_t ring[WGeo<FMT>::kSlots * WGeo<FMT>::kSlot];
+  uint8_t ring[WGeo::kSlots * WGeo::kSlot];
   uint8_t ktile[kWStep * kKStride];   // FP16 K of the step being scored, row-major
   uint8_t vtile[kLatent * kVStride];  // FP16 V^T of the step being accumulated, column-major
   uint32_t rowlist[kWMaxChunk];       // 16-byte row addresses of the split's valid entries
@@ -69,15 +68,15 @@ struct WShared {
 // group G holds, after S^T, the scores of rows 4G..4G+3 of row tile 0 and of row tile 1.
 __device__ __forceinline__ int wide_pv_row(int G, int j) { return (j < 4 ? 4 * G + j : 12 + 4 * G + j); }
 
-template <int HT, int FMT, bool DENSE>
+template <int HT>
 __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a) {
-  using G = WGeo<FMT>;
+  using G = WGeo;
   constexpr int ROWB = G::kRowBytes;
   constexpr int RS = G::kStride;
   constexpr int NL = G::kLoads;
   constexpr int NS = G::kSlots;
   constexpr int NHW = 16 * HT;  // heads per wave
-  __shared__ __attribute__((aligned(16))) WShared<FMT> sh;
+  __shared__ __attribute__((aligned(16))) WShared sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,14 +105,11 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   // kernel: page-table entries staged in LDS in the same memory round trip as the list entries,
   // invalid entries dropped, order kept)
   const int e0 = s * a.chunk;
-  const int p0 = DENSE ? (e0 >> 6) : 0;
-  int npg = DENSE ? (int)(((int64_t)e0 + a.chunk - 1) / 64 - p0 + 1) : (int)a.bt_stride;
-  if (p0 + npg > a.bt_stride) npg = (int)a.bt_stride - p0;
-  if (npg < 0) npg = 0;
+  const int npg = (int)a.bt_stride;
   constexpr int kBtCap = NS * G::kSlot / 4;
   const bool staged = npg <= kBtCap;
   int* btl = reinterpret_cast<int*>(sh.ring);
-  const int* btg = a.block_table + (int64_t)b * a.bt_stride + p0;
+  const int* btg = a.block_table + (int64_t)b * a.bt_stride;
   constexpr int kBtPer = 12;  // entries per thread loaded before any is stored (tables up to 3,072 pages)
   const bool bt_regs = npg <= kWThreads * kBtPer;
   int btv[kBtPer];
@@ -123,8 +119,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   }
   const int L = a.ctx[b];
   const int lim = a.causal ? L - a.T + t : L - 1;
-  const int e_end = DENSE ? (lim + 1 < a.entries ? lim + 1 : a.entries) : a.entries;
-  const int e1 = (e0 + a.chunk < e_end) ? e0 + a.chunk : e_end;
+  const int e1 = (e0 + a.chunk < a.entries) ? e0 + a.chunk : a.entries;
 
   constexpr int EPT = kWEntriesPerThread;
   int pos[EPT];
@@ -132,22 +127,17 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   for (int k = 0; k < EPT; ++k) pos[k] = -1;
   if (e1 > e0) {
     const int ebase = e0 + EPT * tid;
-    if (DENSE) {
+    const int* ip = a.indices + (int64_t)qtok * a.entries + ebase;
+    if (((uintptr_t)a.indices & 15) == 0 && (((int64_t)qtok * a.entries + e0) & 3) == 0 && ebase + EPT <= e1) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ebase + k : -1;
-    } else {
-      const int* ip = a.indices + (int64_t)qtok * a.entries + ebase;
-      if (((uintptr_t)a.indices & 15) == 0 && (((int64_t)qtok * a.entries + e0) & 3) == 0 && ebase + EPT <= e1) {
+      for (int h = 0; h < EPT / 4; ++h) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ip + 4 * h);
 #pragma unroll
-        for (int h = 0; h < EPT / 4; ++h) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(ip + 4 * h);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) pos[4 * h + k] = (int)x[k];
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
+        for (int k = 0; k < 4; ++k) pos[4 * h + k] = (int)x[k];
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
     }
   }
   if (bt_regs) {
@@ -164,9 +154,9 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int pg = (pos[k] >= 0 ? pos[k] : 0) >> 6;
-    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg - p0 < npg;
+    const bool inr = pos[k] >= 0 && pos[k] <= lim && pg < npg;
     int page = -1;
-    if (inr) page = staged ? btl[pg - p0] : btg[pg - p0];
+    if (inr) page = staged ? btl[pg] : btg[pg];
     const bool ok = inr && page >= 0 && page < a.num_pages;
     addr[k] = ok ? (uint32_t)(((uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(pos[k] & 63) * ROWB) >> 4) : 0u;
     vmask |= (uint32_t)ok << k;
@@ -219,35 +209,23 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
 
   // K tile of one step, in pieces that the MFMA loop of phase 2 interleaves: thread tid dequantizes
   // row tid/8, 16-byte chunks c8 + 8i (piece i < 8) of the latent and, as piece 8, the rope dims
-  // 512 + 8*c8 .. +7.  kin holds the raw words (FP8: 8 byte-pairs of the latent, then the rope).
+  // 512 + 8*c8 .. +7.  kin holds the raw words: the latent's nibble dwords, the scale dwords, the rope.
   const int kr_row = tid >> 3, c8 = tid & 7;
   uint8_t* const krow = sh.ktile + kr_row * kKStride;
   auto k_load = [&](int st, uint32_t (&kin)[18]) {
     const uint8_t* rr = slot_ptr(st) + kr_row * RS;
-    if constexpr (FMT == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kin[i] = *reinterpret_cast<const uint32_t*>(rr + 4 * (c8 + 8 * i));
-      const u32x4 sc0 = *reinterpret_cast<const u32x4*>(rr + 256);
-      const u32x4 sc1 = *reinterpret_cast<const u32x4*>(rr + 272);
+    for (int i = 0; i < 8; ++i) kin[i] = *reinterpret_cast<const uint32_t*>(rr + 4 * (c8 + 8 * i));
+    const u32x4 sc0 = *reinterpret_cast<const u32x4*>(rr + 256);
+    const u32x4 sc1 = *reinterpret_cast<const u32x4*>(rr + 272);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kin[8 + i] = sc0[i];
-        kin[12 + i] = sc1[i];
-      }
-      const u32x2 rp = *reinterpret_cast<const u32x2*>(rr + 288 + 8 * c8);
-      kin[16] = rp[0];
-      kin[17] = rp[1];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(rr + 8 * (c8 + 8 * i));
-        kin[2 * i] = x[0];
-        kin[2 * i + 1] = x[1];
-      }
-      const u32x2 rp = *reinterpret_cast<const u32x2*>(rr + kLatent + 8 * c8);
-      kin[16] = rp[0];
-      kin[17] = rp[1];
+    for (int i = 0; i < 4; ++i) {
+      kin[8 + i] = sc0[i];
+      kin[12 + i] = sc1[i];
     }
+    const u32x2 rp = *reinterpret_cast<const u32x2*>(rr + 288 + 8 * c8);
+    kin[16] = rp[0];
+    kin[17] = rp[1];
   };
   auto k_piece = [&](int i, const uint32_t (&kin)[18]) {
     if (i == 8) {
@@ -257,16 +235,12 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
       return;
     }
     f16x8 v;
-    if constexpr (FMT == 0) {
-      // block of chunk c8 + 8i is (c8 >> 1) + 4i: byte c8 >> 1 of scale dword i, broadcast to a pair
-      const uint32_t sd = kin[8 + i];
-      const f16x2 ss = e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sd, sd, (uint32_t)(c8 >> 1) * 0x0101u));
-      v = as_f16x8(fp4x2_to_f16<0>(kin[i]) * ss, fp4x2_to_f16<1>(kin[i]) * ss, fp4x2_to_f16<2>(kin[i]) * ss,
-                   fp4x2_to_f16<3>(kin[i]) * ss);
-    } else {
-      v = as_f16x8(e4m3x2_to_f16<false>(kin[2 * i]), e4m3x2_to_f16<true>(kin[2 * i]),
-                   e4m3x2_to_f16<false>(kin[2 * i + 1]), e4m3x2_to_f16<true>(kin[2 * i + 1]));
-    }
+    // block of chunk c8 + 8i is (c8 >> 1) + 4i: byte c8 >> 1 of scale dword i, broadcast to a pair
+    const uint32_t sd = kin[8 + i];
+    const f16x2 ss = e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sd, sd, (uint32_t)(c8 >> 1) * 0x0101u));
+    v = as_f16x8(fp4x2_to_f16<0>(kin[i]) * ss, fp4x2_to_f16<1>(kin[i]) * ss, fp4x2_to_f16<2>(kin[i]) * ss,
+                 fp4x2_to_f16<3>(kin[i]) * ss);
+
     *reinterpret_cast<f16x8*>(krow + 16 * (c8 + 8 * i)) = v;
   };
 
@@ -280,62 +254,38 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint8_t* ra = slot + wide_pv_row(Gq, 2 * p) * RS;
-      if constexpr (FMT == 0) {
-        vin[4 * p + 0] = *reinterpret_cast<const uint32_t*>(ra + 4 * co);
-        vin[4 * p + 1] = *reinterpret_cast<const uint32_t*>(ra + RS + 4 * co);
-        vin[4 * p + 2] = *reinterpret_cast<const uint32_t*>(ra + 256 + 4 * (co >> 3));
-        vin[4 * p + 3] = *reinterpret_cast<const uint32_t*>(ra + RS + 256 + 4 * (co >> 3));
-      } else {
-        const u32x2 da = *reinterpret_cast<const u32x2*>(ra + 8 * co);
-        const u32x2 db = *reinterpret_cast<const u32x2*>(ra + RS + 8 * co);
-        vin[4 * p + 0] = da[0];
-        vin[4 * p + 1] = da[1];
-        vin[4 * p + 2] = db[0];
-        vin[4 * p + 3] = db[1];
-      }
+      vin[4 * p + 0] = *reinterpret_cast<const uint32_t*>(ra + 4 * co);
+      vin[4 * p + 1] = *reinterpret_cast<const uint32_t*>(ra + RS + 4 * co);
+      vin[4 * p + 2] = *reinterpret_cast<const uint32_t*>(ra + 256 + 4 * (co >> 3));
+      vin[4 * p + 3] = *reinterpret_cast<const uint32_t*>(ra + RS + 256 + 4 * (co >> 3));
     }
   };
-  // vpr[p][0..3]: NVFP4 -> the two nibble interleaves (even, odd columns) and the scale pair;
-  // FP8 -> the byte interleaves of columns (0,1), (2,3), (4,5), (6,7)
-  auto v_prep = [&](const uint32_t (&vin)[16], uint32_t (&vpr)[4][4]) {
+  // vpr[p][0..2]: the two nibble interleaves (even, odd columns) of rows (a, b) and their scale pair
+  auto v_prep = [&](const uint32_t (&vin)[16], uint32_t (&vpr)[4][3]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      if constexpr (FMT == 0) {
-        const uint32_t bsel = (uint32_t)((co >> 1) & 3);
-        const uint32_t da = vin[4 * p], db = vin[4 * p + 1], sa = vin[4 * p + 2], sb = vin[4 * p + 3];
-        vpr[p][0] = nib_pair<0>(da, db);
-        vpr[p][1] = nib_pair<1>(da, db);
-        // block scales of rows a and b as an FP16 pair
-        vpr[p][2] = __builtin_bit_cast(uint32_t, e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sb, sa, bsel | ((4 + bsel) << 8))));
-        vpr[p][3] = 0;
-      } else {
-        const uint32_t a0 = vin[4 * p], a1 = vin[4 * p + 1], b0 = vin[4 * p + 2], b1 = vin[4 * p + 3];
-        vpr[p][0] = __builtin_amdgcn_perm(b0, a0, 0x05010400u);  // columns 0, 1
-        vpr[p][1] = __builtin_amdgcn_perm(b0, a0, 0x07030602u);  // columns 2, 3
-        vpr[p][2] = __builtin_amdgcn_perm(b1, a1, 0x05010400u);  // columns 4, 5
-        vpr[p][3] = __builtin_amdgcn_perm(b1, a1, 0x07030602u);  // columns 6, 7
-      }
+      const uint32_t bsel = (uint32_t)((co >> 1) & 3);
+      const uint32_t da = vin[4 * p], db = vin[4 * p + 1], sa = vin[4 * p + 2], sb = vin[4 * p + 3];
+      vpr[p][0] = nib_pair<0>(da, db);
+      vpr[p][1] = nib_pair<1>(da, db);
+      // block scales of rows a and b as an FP16 pair
+      vpr[p][2] = __builtin_bit_cast(uint32_t, e4m3x2_to_f16<false>(__builtin_amdgcn_perm(sb, sa, bsel | ((4 + bsel) << 8))));
     }
   };
-  auto v_piece = [&](int c, const uint32_t (&vpr)[4][4]) {
+  auto v_piece = [&](int c, const uint32_t (&vpr)[4][3]) {
     f16x2 v[4];  // FP16 pairs (row a, row b) of column c
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      if constexpr (FMT == 0) {
-        const uint32_t e = vpr[p][c & 1];
-        const f16x2 sp = __builtin_bit_cast(f16x2, vpr[p][2]);
-        f16x2 x;
-        switch (c >> 1) {
-          case 0: x = fp4x2_to_f16<0>(e); break;
-          case 1: x = fp4x2_to_f16<1>(e); break;
-          case 2: x = fp4x2_to_f16<2>(e); break;
-          default: x = fp4x2_to_f16<3>(e); break;
-        }
-        v[p] = x * sp;
-      } else {
-        const uint32_t e = vpr[p][c >> 1];
-        v[p] = (c & 1) ? e4m3x2_to_f16<true>(e) : e4m3x2_to_f16<false>(e);
+      const uint32_t e = vpr[p][c & 1];
+      const f16x2 sp = __builtin_bit_cast(f16x2, vpr[p][2]);
+      f16x2 x;
+      switch (c >> 1) {
+        case 0: x = fp4x2_to_f16<0>(e); break;
+        case 1: x = fp4x2_to_f16<1>(e); break;
+        case 2: x = fp4x2_to_f16<2>(e); break;
+        default: x = fp4x2_to_f16<3>(e); break;
       }
+      v[p] = x * sp;
     }
     *reinterpret_cast<f16x8*>(sh.vtile + (8 * co + c) * kVStride + 16 * Gq) = as_f16x8(v[0], v[1], v[2], v[3]);
   };
@@ -399,7 +349,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
       for (int tt = 0; tt < HT; ++tt) sacc[rt][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     {
       uint32_t vin[16];
-      uint32_t vpr[4][4];
+      uint32_t vpr[4][3];
       v_load(k, vin);
       auto ka = [&](int ks, int rt) {
         return *reinterpret_cast<const f16x8*>(sh.ktile + (16 * rt + n) * kKStride + 2 * (32 * ks + 8 * g));
@@ -572,7 +522,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   // The splits are added in their order, this workgroup's own result rounded to FP16 as the stored ones
   // are, so the merged bits do not depend on which split's workgroup merges.
   float* wts = reinterpret_cast<float*>(sh.ring);
-  static_assert(kWWaves * 2 * 16 * 64 * 4 <= WGeo<FMT>::kSlots * WGeo<FMT>::kSlot, "merge weights fit the ring");
+  static_assert(kWWaves * 2 * 16 * 64 * 4 <= WGeo::kSlots * WGeo::kSlot, "merge weights fit the ring");
 #pragma unroll
   for (int tt = 0; tt < HT; ++tt) {
     const int64_t hrow = (int64_t)qtok * a.H + hw0 + 16 * tt + n;
@@ -615,10 +565,10 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int HT, int FMT, bool DENSE>
+template <int HT>
 void launch_wide_one(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.B * a.T * a.splits);
-  hipLaunchKernelGGL((decode_wide_kernel<HT, FMT, DENSE>), dim3(grid), dim3(kWThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_wide_kernel<HT>), dim3(grid), dim3(kWThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -626,8 +576,8 @@ void launch_wide_one(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream) {
   // NVFP4 rows and sparse lists only (uses_wide_kernel); other formats run the 32-head-group kernel
   if (fmt != 0 || a.indices == nullptr || (a.H != 64 && a.H != 128)) return hipErrorInvalidValue;
-  if (a.H == 64) launch_wide_one<1, 0, false>(a, stream);
-  else launch_wide_one<2, 0, false>(a, stream);
+  if (a.H == 64) launch_wide_one<1>(a, stream);
+  else launch_wide_one<2>(a, stream);
   return hipGetLastError();
 }
 
