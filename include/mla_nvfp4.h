@@ -159,6 +159,31 @@ int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes
                       size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step of a layer in one launch: the quantize-on-write of each query token's own new row, then
+ * mla_sparse_decode over the cache with those rows in it (the pages' decode step writes the new token's
+ * row into the NVFP4 cache, then attends over the selected rows).  Token t of request b is position
+ * p = context_lens[b] - T + t, so its row goes to slot block_table[b*bt_stride + p/64]*64 + p%64; the
+ * results (out, lse and the pool's bytes) are those of mla_kv_quant_nvfp4 of the B*T rows at these slots
+ * followed by mla_sparse_decode with the same arguments.  A row whose position is negative, beyond the
+ * table width, or on a page entry outside [0, num_pages) is not written (the writer skips such slots, and
+ * the decode selects nothing there).
+ *   k_nope, k_rope  (device) bf16 new rows [B*T, nope_stride] and [B*T, rope_stride] (row b*T + t), 512 and
+ *                   64 values used, as for mla_kv_quant_nvfp4: strides >= 512 / >= 64, multiples of 8,
+ *                   pointers 16-byte aligned
+ *   pool            (device, written) the NVFP4 page pool
+ *   other arguments, the workspace, the split choice and errors as for mla_sparse_decode.
+ * Every workgroup of request b writes all T rows of the request (the same bytes) and waits for its stores
+ * before its first gather, so no workgroup reads a row before it is written; other requests' lists
+ * must not select these slots in the same call (they may read the old or the new bytes).
+ */
+int mla_sparse_decode_append(const void* q, void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                             const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                             const int32_t* indices, const void* k_nope, int64_t nope_stride, const void* k_rope,
+                             int64_t rope_stride, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                             int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * mla_sparse_decode without a workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It runs the same
  * kernels with the same split choice (same results, bit for bit) and allocates nothing: the split

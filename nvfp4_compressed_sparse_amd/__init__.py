@@ -23,7 +23,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_STRIDE
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_kv_quant_nvfp4", "mla_kv_quant_fp8", "mla_sparse_decode_splits",
     "mla_dense_decode_splits", "mla_sparse_decode_workspace_bytes", "mla_dense_decode_workspace_bytes",
-    "mla_sparse_decode", "mla_sparse_decode_fp8_splits", "mla_sparse_decode_fp8_workspace_bytes",
+    "mla_sparse_decode", "mla_sparse_decode_append", "mla_sparse_decode_fp8_splits", "mla_sparse_decode_fp8_workspace_bytes",
     "mla_sparse_decode_fp8", "mla_noalloc_scratch_bytes", "mla_sparse_decode_noalloc", "mla_dense_decode_fp8", "mla_stage_nvfp4_fp8", "mla_kv_quant_pth",
     "mla_sparse_decode_pth_workspace_bytes", "mla_sparse_decode_pth", "mla_index_key_quant", "mla_index_logits",
     "mla_index_topk_workspace_bytes", "mla_index_topk",
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         "mla_dense_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "mla_sparse_decode": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                              sz, P]),
+        "mla_sparse_decode_append": (ctypes.c_int, [P, P, i64, i64, P, i64, P, P, P, i64, P, i64, i32, i32, i32, i32,
+                                                    f, i32, i32, P, P, P, sz, P]),
         "mla_dense_decode_fp8": (ctypes.c_int, [P, P, i64, i64, P, i64, P, i32, i32, i32, i32, f, i32, i32, P, P, P,
                                                 sz, P]),
         "mla_sparse_decode_fp8_splits": (ctypes.c_int, [i32, i32, i32, i32]),
@@ -258,6 +260,36 @@ def mla_sparse_decode(q, pool, page_stride_bytes, num_pages, block_table, contex
     """Sparse MLA decode over NVFP4 rows; returns (out [B,T,H,512] bf16, lse or None)."""
     return _sparse("mla_sparse_decode", "mla_sparse_decode_workspace_bytes", q, pool, page_stride_bytes, num_pages,
                    block_table, context_lens, indices, sm_scale, causal, num_splits, out, lse, workspace, stream)
+
+
+def mla_sparse_decode_append(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, k_nope, k_rope,
+                             sm_scale, causal=False, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """One decode step in one launch: each query token's new row (k_nope [B*T, 512], k_rope [B*T, 64] bf16,
+    row b*T + t) written at position context_lens[b] - T + t, then mla_sparse_decode over the cache with
+    those rows in it; returns (out, lse).  The pool is written."""
+    import torch
+    _common(q, pool, block_table, context_lens)
+    _dev(indices, torch.int32, "indices")
+    _dev(k_nope, torch.bfloat16, "k_nope")
+    _dev(k_rope, torch.bfloat16, "k_rope")
+    B, T, H, _ = q.shape
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (B, T) or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [B, T, topk] int32 tensor")
+    if k_nope.dim() != 2 or tuple(k_nope.shape) != (B * T, LATENT_DIM) or k_nope.stride(1) != 1:
+        raise ValueError("k_nope must be [B*T, 512] with unit inner stride")
+    if k_rope.dim() != 2 or tuple(k_rope.shape) != (B * T, ROPE_DIM) or k_rope.stride(1) != 1:
+        raise ValueError("k_rope must be [B*T, 64] with unit inner stride")
+    topk = indices.shape[2]
+    ws = lib().mla_sparse_decode_workspace_bytes(B, T, H, topk, int(num_splits))
+    out, lse, workspace = _decode_io(q, out, lse, workspace, ws)
+    st = _call("mla_sparse_decode_append", q.data_ptr(), pool.data_ptr(), int(page_stride_bytes), int(num_pages),
+               block_table.data_ptr(), block_table.stride(0), context_lens.data_ptr(), indices.data_ptr(),
+               k_nope.data_ptr(), k_nope.stride(0), k_rope.data_ptr(), k_rope.stride(0), B, T, H, topk,
+               float(sm_scale), int(bool(causal)), int(num_splits), out.data_ptr(),
+               None if lse is None else lse.data_ptr(), None if workspace is None else workspace.data_ptr(),
+               0 if workspace is None else workspace.numel(), _stream(stream))
+    _check("mla_sparse_decode_append", st)
+    return out, lse
 
 
 def mla_sparse_decode_fp8(q, pool, page_stride_bytes, num_pages, block_table, context_lens, indices, sm_scale,

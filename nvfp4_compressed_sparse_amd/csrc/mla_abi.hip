@@ -150,10 +150,18 @@ int check_decode_common(const void* q, const void* pool, int64_t page_stride, in
   return MLA_OK;
 }
 
+// The new rows of mla_sparse_decode_append (bf16, row strides in elements).
+struct AppendRows {
+  const void* k_nope;
+  int64_t nope_stride;
+  const void* k_rope;
+  int64_t rope_stride;
+};
+
 int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, int64_t num_pages,
                const int32_t* block_table, int64_t bt_stride, const int32_t* ctx, const int32_t* indices, int32_t B,
                int32_t T, int32_t H, int32_t entries, float sm_scale, int32_t causal, int32_t num_splits, void* out,
-               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+               float* lse, void* workspace, size_t workspace_bytes, void* stream, const AppendRows* app = nullptr) {
   int S = num_splits;
   int chunk = (int)ceil_div(entries, S);
   // a dense split starts on a page boundary, so that each 64-row step of the decoder is one page
@@ -192,6 +200,13 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   a.part_o = need ? (uint16_t*)((char*)workspace + wl.o_off) : nullptr;
   a.part_lse = need ? (float*)((char*)workspace + wl.lse_off) : nullptr;
   a.counters = need ? (int*)((char*)workspace + wl.cnt_off) : nullptr;
+  if (app) {
+    a.new_nope = (const uint16_t*)app->k_nope;
+    a.new_nope_stride = app->nope_stride;
+    a.new_rope = (const uint16_t*)app->k_rope;
+    a.new_rope_stride = app->rope_stride;
+    a.wpool = (uint8_t*)const_cast<void*>(pool);
+  }
   return mla::launch_decode(fmt, a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -311,6 +326,28 @@ int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes
   int S = num_splits ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
   return run_decode(0, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
                     topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_sparse_decode_append(const void* q, void* pool, int64_t page_stride_bytes, int64_t num_pages,
+                             const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                             const int32_t* indices, const void* k_nope, int64_t nope_stride, const void* k_rope,
+                             int64_t rope_stride, int32_t B, int32_t T, int32_t H, int32_t topk, float sm_scale,
+                             int32_t causal, int32_t num_splits, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, B, T, H,
+                               sm_scale, causal, out, MLA_NVFP4_ROW_BYTES);
+  if (st != MLA_OK) return st;
+  if (!indices || !k_nope || !k_rope) return MLA_ERR_NULL;
+  if (!aligned(indices, 4)) return MLA_ERR_STRIDE_ALIGN;
+  // the new rows as the writer takes them: 16-byte aligned bf16 rows of at least 512 and 64 values
+  if (nope_stride < 512 || rope_stride < 64 || nope_stride % 8 || rope_stride % 8) return MLA_ERR_STRIDE_ALIGN;
+  if (!aligned(k_nope, 16) || !aligned(k_rope, 16)) return MLA_ERR_STRIDE_ALIGN;
+  if (topk < 1 || topk > MLA_MAX_TOPK) return MLA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return MLA_ERR_SHAPE;
+  int S = num_splits ? num_splits : mla_sparse_decode_splits(B, T, H, topk);
+  const AppendRows app{k_nope, nope_stride, k_rope, rope_stride};
+  return run_decode(0, q, pool, page_stride_bytes, num_pages, block_table, bt_stride, context_lens, indices, B, T, H,
+                    topk, sm_scale, causal, S, out, lse, workspace, workspace_bytes, stream, &app);
 }
 
 int mla_sparse_decode_fp8(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,

@@ -164,6 +164,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // append: wave w holds new row w of the request (the bf16 input, loaded with the prologue's loads);
+  // rows w + 8i, when T > 8, are loaded where they are written
+  const bool append = !DENSE && a.new_nope != nullptr;
+  u32x4 nraw = u32x4{0u, 0u, 0u, 0u};
+  uint32_t nrope = 0;
+  if (append && w < a.T) {
+    const int64_t nr = (int64_t)b * a.T + w;
+    nraw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+    nrope = a.new_rope[nr * a.new_rope_stride + lane];
+  }
+
   const int e0 = s * a.chunk;
   const int* btg = a.block_table + (int64_t)b * a.bt_stride;
   const int L = a.ctx[b];
@@ -238,6 +249,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int i = tid; i < npg; i += kThreads) btl[i] = btg[i];
   }
   __syncthreads();  // staged page-table entries visible
+
+  if (append) {
+    // the request's new rows at positions L - T + r, quantized and written to the pool by one wave each
+    // (a position before the start of the context, beyond the table width or on a page outside the
+    // pool is not written, as the writer skips such slots); the stores are complete before any gather
+    // (the wait before the row list's barrier)
+    for (int r = w; r < a.T; r += kWaves) {
+      u32x4 raw = nraw;
+      uint32_t rope = nrope;
+      if (r >= kWaves) {
+        const int64_t nr = (int64_t)b * a.T + r;
+        raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+        rope = a.new_rope[nr * a.new_rope_stride + lane];
+      }
+      const int p = L - a.T + r;
+      if (p < 0 || (p >> 6) >= npg) continue;
+      const int page = staged ? btl[p >> 6] : btg[p >> 6];
+      if (page < 0 || page >= a.num_pages) continue;
+      quant_row_wave<FMT>(raw, rope, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB,
+                          lane);
+    }
+  }
 
   // a position past the limit, or on a page beyond the table width (only with a context longer than
   // the table allows), selects nothing; every table read of the lane is issued before any is used

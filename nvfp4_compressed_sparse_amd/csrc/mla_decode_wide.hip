@@ -101,6 +101,17 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
         qraw[tt][ks] = *reinterpret_cast<const u32x4*>(qb + (int64_t)16 * tt * kQK + 32 * ks);
   }
 
+  // append (as in the 16/32-head kernel): wave w holds new row w of the request; rows w + 4i, when T > 4,
+  // are loaded where they are written
+  const bool append = a.new_nope != nullptr;
+  u32x4 nraw = u32x4{0u, 0u, 0u, 0u};
+  uint32_t nrope = 0;
+  if (append && w < a.T) {
+    const int64_t nr = (int64_t)b * a.T + w;
+    nraw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+    nrope = a.new_rope[nr * a.new_rope_stride + lane];
+  }
+
   // ---- prologue: valid rows of this split -> LDS list of 16-byte row addresses (as in the 16/32-head
   // kernel: page-table entries staged in LDS in the same memory round trip as the list entries,
   // invalid entries dropped, order kept)
@@ -148,6 +159,25 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
     for (int i = tid; i < npg; i += kWThreads) btl[i] = btg[i];
   }
   __syncthreads();  // staged page-table entries visible
+
+  if (append) {
+    // the request's new rows at positions L - T + r, written by one wave each (skipped where the writer
+    // would skip the slot); complete before any gather (the wait before the row list's barrier)
+    for (int r = w; r < a.T; r += kWWaves) {
+      u32x4 raw = nraw;
+      uint32_t rope = nrope;
+      if (r >= kWWaves) {
+        const int64_t nr = (int64_t)b * a.T + r;
+        raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+        rope = a.new_rope[nr * a.new_rope_stride + lane];
+      }
+      const int p = L - a.T + r;
+      if (p < 0 || (p >> 6) >= npg) continue;
+      const int page = staged ? btl[p >> 6] : btg[p >> 6];
+      if (page < 0 || page >= a.num_pages) continue;
+      quant_row_wave<0>(raw, rope, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB, lane);
+    }
+  }
 
   uint32_t addr[EPT];
   uint32_t vmask = 0;

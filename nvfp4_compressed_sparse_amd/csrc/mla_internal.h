@@ -39,6 +39,14 @@ struct DecodeArgs {
   uint16_t* part_o;           // FP16 [B*T*H, S, 512] when S > 1
   float* part_lse;            // [B*T*H, S]
   int* counters;              // [B*T*head groups] split arrival counters, zero between calls
+  // append (mla_sparse_decode_append): the B*T new rows, token t of request b written at position
+  // ctx[b] - T + t before any row is read; every workgroup of request b writes all T of them (the same
+  // bytes), so each has them in memory before its own gathers.  nullptr otherwise.
+  const uint16_t* new_nope = nullptr;  // [B*T rows, new_nope_stride] bf16, 512 used
+  int64_t new_nope_stride = 0;
+  const uint16_t* new_rope = nullptr;  // [B*T rows, new_rope_stride] bf16, 64 used
+  int64_t new_rope_stride = 0;
+  uint8_t* wpool = nullptr;            // the pool, writable (the memory of pool)
 };
 
 struct StageArgs {

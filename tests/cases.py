@@ -112,15 +112,17 @@ class Case:
         return oracle.dense_decode_fp8(self.q, pool, c.page_stride, self.lay.num_pages, self.lay.block_table,
                                        self.lay.ctx, c.sm_scale, c.causal, units=units)[:2]
 
-    def vmax(self, idx=None):
-        """Largest |V| per query token and latent column among its selected rows: [B*T, 1, 512]."""
+    def vmax(self, idx=None, ctx=None):
+        """Largest |V| per query token and latent column among its selected rows (under context lengths
+        ctx, the case's own by default): [B*T, 1, 512]."""
         c = self.cfg
         pool = self.oracle_pool()
         idx = (self.idx if idx is None else idx) if c.topk else None
         out = np.zeros((c.B * c.T, 1, 512))
         for b in range(c.B):
             for t in range(c.T):
-                pos = selected_positions(self.lay.ctx, c.T, c.causal, idx, b, t, self.lay.block_table,
+                pos = selected_positions(self.lay.ctx if ctx is None else ctx, c.T, c.causal, idx, b, t,
+                                         self.lay.block_table,
                                          self.lay.num_pages)
                 if pos.size == 0:
                     continue

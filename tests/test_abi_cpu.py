@@ -367,3 +367,41 @@ def test_pth_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert quant() == 5 and dec(S=2, wsb=need) == 5
+
+
+def test_sparse_decode_append_argument_errors():
+    def call(**kw):
+        a = dict(q=FAKE, pool=FAKE, ps=64 * 352, npg=10, bt=FAKE, bts=4, ctx=FAKE, idx=FAKE, kn=FAKE, kns=512,
+                 kr=FAKE, krs=64, B=2, T=1, H=16, k=256, sc=0.07, causal=0, S=0, out=FAKE, lse=None, ws=None, wsb=0,
+                 stream=None)
+        a.update(kw)
+        return M.lib().mla_sparse_decode_append(a["q"], a["pool"], a["ps"], a["npg"], a["bt"], a["bts"], a["ctx"],
+                                                a["idx"], a["kn"], a["kns"], a["kr"], a["krs"], a["B"], a["T"],
+                                                a["H"], a["k"], a["sc"], a["causal"], a["S"], a["out"], a["lse"],
+                                                a["ws"], a["wsb"], a["stream"])
+    assert call(q=None) == 1
+    assert call(pool=None) == 1
+    assert call(idx=None) == 1
+    assert call(kn=None) == 1
+    assert call(kr=None) == 1
+    assert call(B=0) == 2
+    assert call(H=48) == 2
+    assert call(k=2049) == 2
+    assert call(S=65) == 2
+    assert call(causal=2) == 2
+    assert call(sc=float("nan")) == 2
+    assert call(ps=64 * 576 + 8) == 3
+    assert call(kns=504) == 3  # rows shorter than 512 values
+    assert call(krs=60) == 3
+    assert call(kns=520 + 4) == 3  # not a multiple of 16 bytes
+    assert call(kn=FAKE + 8) == 3
+    assert call(kr=FAKE + 2) == 3
+    need = M.lib().mla_sparse_decode_workspace_bytes(2, 1, 16, 256, 4)
+    assert call(S=4) == 1
+    assert call(S=4, ws=FAKE, wsb=need - 1) == 4
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == 5
+        need4 = M.lib().mla_sparse_decode_workspace_bytes(2, 4, 16, 256, 4)
+        assert call(S=4, ws=FAKE, wsb=need4 - 1, T=4, causal=1) == 4
+        assert call(S=4, ws=FAKE, wsb=need4, T=4, causal=1) == 5
