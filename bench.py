@@ -63,11 +63,11 @@ def source_hash(cfg):
     return h.hexdigest()[:16]
 
 
-def profile_record(cfg, kind: str, key: str):
+def profile_record(cfg, kind: str, key: str, variant: str = ""):
     """A figure from a rocprofv3 counter summary of this workload's decode kernel, if it was taken on the
-    current kernel source: profiles/decode_<workload>_<kind>.md holds lines `source_hash: ...` and
+    current kernel source: profiles/decode_<workload><variant>_<kind>.md holds lines `source_hash: ...` and
     `<key>: ...`."""
-    p = os.path.join(ROOT, "profiles", f"decode_{cfg.name}_{kind}.md")
+    p = os.path.join(ROOT, "profiles", f"decode_{cfg.name}{variant}_{kind}.md")
     if not os.path.exists(p):
         return None
     rec = {}
@@ -109,6 +109,9 @@ def main():
                          "to an FP8 copy, then the FP8 decoder reads it), or the per-token-head FP8 layout "
                          "(FP8 latent, fp32 scale, bf16 rope in three buffers) and its decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="sparse NVFP4 decode: write the step's new rows with the writer's own launch before the "
+                         "decode (two launches per step) instead of inside the decode launch")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable-rate probes (streaming read, row gather, MFMA loop) run after the timing")
     ap.add_argument("--graph", action="store_true",
@@ -189,6 +192,9 @@ def main():
     q_sets, idx_sets = inp["q_sets"], inp["idx_sets"]
     sparse_fp8 = bool(cfg.topk) and cfg.fmt == "fp8"  # the FP8-cache arm of the pages' comparison
     sparse_fn = M.mla_sparse_decode_fp8 if sparse_fp8 else M.mla_sparse_decode
+    # the sparse NVFP4 step in one launch: the decode kernel writes the step's new rows in its prologue
+    fusable = bool(cfg.topk) and not sparse_fp8 and not cfg.quant_chunk and not staged_path and not pth_path
+    fused = fusable and not args.unfused
     if cfg.topk:
         S = args.splits or (M.mla_sparse_decode_fp8_splits if sparse_fp8 else M.mla_sparse_decode_splits)(
             cfg.B, cfg.T, cfg.H, cfg.topk)
@@ -255,6 +261,10 @@ def main():
             M.mla_dense_decode_fp8(q_sets[k].view(nq, 1, cfg.H, 576), staged, 64 * 576, nq * st_pages, st_bt, st_len,
                                    st_pages * 64, cfg.sm_scale, num_splits=S, out=out1, lse=lse1, workspace=ws,
                                    stream=st)
+        elif fused:
+            M.mla_sparse_decode_append(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"],
+                                       idx_sets[k], w_lat, w_rope, cfg.sm_scale, causal=cfg.causal, num_splits=S,
+                                       out=out, lse=lse, workspace=ws, stream=st)
         elif cfg.topk:
             sparse_fn(q_sets[k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_sets[k], cfg.sm_scale,
                       causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=st)
@@ -264,16 +274,19 @@ def main():
                                    stream=st)
 
     for i in range(args.warmup):
-        write(i)
+        if not fused:
+            write(i)
         decode(i)
     torch.cuda.synchronize()
     if args.graph:
         # The step's calls captured once as HIP graphs (the write, and the decode of each index set) and replayed.
         # Nothing in a captured call allocates or clears memory (the split counters return to zero inside the
         # decode kernel).  Measured slower than the prepared launches below on this software stack.
-        g_write = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_write):
-            write(0)
+        g_write = None
+        if not fused:
+            g_write = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_write):
+                write(0)
         g_dec = []
         for k in range(N_SETS):
             g = torch.cuda.CUDAGraph()
@@ -282,12 +295,14 @@ def main():
             g_dec.append(g)
         torch.cuda.synchronize()
         for i in range(max(args.warmup, N_SETS)):
-            g_write.replay()
+            if g_write is not None:
+                g_write.replay()
             g_dec[i % N_SETS].replay()
         torch.cuda.synchronize()
 
         def step(i):
-            g_write.replay()
+            if g_write is not None:
+                g_write.replay()
             g_dec[i % N_SETS].replay()
 
         def dec_call(i):
@@ -296,11 +311,12 @@ def main():
         # The step's calls with their arguments checked and converted once (the binding's prepared calls): each
         # step then costs the host two plain C-ABI calls, so the host stays ahead of the GPU and the timed loop
         # measures the GPU rather than the host's launch path.
-        w_call = M.prepare(write, 0)
+        w_call = None if fused else M.prepare(write, 0)
         d_calls = [M.prepare(decode, k) for k in range(N_SETS)]
 
         def step(i):
-            w_call()
+            if w_call is not None:
+                w_call()
             d_calls[i % N_SETS]()
 
         def dec_call(i):
@@ -335,11 +351,15 @@ def main():
     dec_avg_us = d0.elapsed_time(d1) * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (events), wall {wall / args.steps * 1e6:.2f} "
         f"us/step; decode call avg {dec_avg_us:.2f} us over {args.steps} back-to-back calls")
+    if fused:  # the timed steps are themselves back-to-back launches of the one call
+        dec_avg_us = ms_per_step * 1e3
 
     nq = cfg.B * cfg.T
     value = nq / (ms_per_step * 1e-3)
     vrows = float(np.mean([valid[i % N_SETS] for i in range(args.steps)]))
     bytes_per, flops_per = algorithmic_work(cfg, vrows)
+    if fused:  # the new rows: bf16 read, quantized row written
+        bytes_per += nq * (1152 + cfg.row_bytes)
     if staged_path:
         # the staged path moves a selected row three times: 352 B read, 576 B FP8 copy written and read
         bytes_per += int(vrows * 2 * 576)
@@ -353,16 +373,22 @@ def main():
         ach = flops_per / (dec_avg_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
-    t = None if (staged_path or pth_path) else profile_record(cfg, "traffic", "traffic_bytes_per_launch")
+    variant = "_unfused" if (fusable and not fused) else ""
+    t = None if (staged_path or pth_path) else profile_record(cfg, "traffic", "traffic_bytes_per_launch", variant)
     roof["traffic"] = None if t is None else int(t)
     if cfg.H > 32:
-        roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent")
+        roof["mfma_util_counter"] = profile_record(cfg, "mfma", "mfma_util_percent", variant)
     if staged_path:
         roof["kernel"] = ("mla_stage_nvfp4_fp8 + mla_dense_decode_fp8 calls: stage_rows_kernel then decode_kernel "
                           "over the FP8 copy, back-to-back calls timed together with HIP events on their stream")
     elif pth_path:
         roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), "
                           "back-to-back calls timed with HIP events on their stream")
+    elif fused:
+        roof["kernel"] = ("mla_sparse_decode_append call: " +
+                          ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") +
+                          " (the step's new rows quantized and written in its prologue, split merge inside), "
+                          "back-to-back calls timed with HIP events on its stream")
     else:
         roof["kernel"] = (("mla_sparse_decode_fp8" if sparse_fp8 else "mla_sparse_decode") if cfg.topk
                           else "mla_dense_decode_fp8") + " call: " + \
@@ -403,8 +429,10 @@ def main():
                    "index_padding": "position 0" if args.pad_as_row0 else "-1 (skipped)",
                    "step": ("quantize %d rows + %s" % (cfg.quant_chunk or nq,
                                                        "stage + FP8 decode" if staged_path else "decode")),
-                   "launch": ("hip graph replay (write graph + decode graph per step)" if args.graph else
-                              "prepared C-ABI calls (arguments checked once), write + decode per step")},
+                   "launch": ("one launch per step (the decode writes the new rows), " if fused else
+                              "write + decode launches per step, ") +
+                             ("hip graph replay" if args.graph else
+                              "prepared C-ABI calls (arguments checked once)")},
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -739,9 +767,15 @@ def bench_dsa_step(args):
         M.mla_index_topk(logits, lens, cfg.topk, out=idx.view(n, cfg.topk), workspace=tk_ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        M.mla_kv_quant_nvfp4(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
-        M.mla_sparse_decode(inp["q_sets"][k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx,
-                            cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws, stream=stream)
+        if args.unfused:
+            M.mla_kv_quant_nvfp4(w_lat, w_rope, w_slots, pool, cfg.page_stride, lay.num_pages, stream=stream)
+            M.mla_sparse_decode(inp["q_sets"][k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx,
+                                cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out, lse=lse, workspace=ws,
+                                stream=stream)
+        else:  # the new rows written by the decode launch itself
+            M.mla_sparse_decode_append(inp["q_sets"][k], pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"],
+                                       idx, w_lat, w_rope, cfg.sm_scale, causal=cfg.causal, num_splits=S, out=out,
+                                       lse=lse, workspace=ws, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 

@@ -164,9 +164,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // append: wave w holds new row w of the request (the bf16 input, loaded with the prologue's loads);
-  // rows w + 8i, when T > 8, are loaded where they are written
-  const bool append = !DENSE && a.new_nope != nullptr;
+  // The fused step (new rows given): wave w quantizes new row w of the request (the bf16 input, loaded
+  // with the prologue's loads) while the page table and the list entries are in flight, and stores it
+  // once the table is staged; rows w + 8i, when T > 8, are loaded and quantized there.  The stores are
+  // complete before any gather (the wait before the row list's barrier).
+  constexpr bool kAppend = FMT == 0 && !DENSE;
+  const bool append = kAppend && a.new_nope != nullptr;
   u32x4 nraw = u32x4{0u, 0u, 0u, 0u};
   uint32_t nrope = 0;
   if (append && w < a.T) {
@@ -241,6 +244,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
     }
   }
+  RowWords nw{0u, 0u, 0u};
+  if (append && w < a.T) {
+    nw = quant_row_words<FMT>(nraw, nrope, lane);
+    // keep the quantization here, ahead of the table's arrival, rather than next to its store
+    asm volatile("" : "+v"(nw.lat0), "+v"(nw.lat1), "+v"(nw.rope));
+  }
   if (bt_regs) {
 #pragma unroll
     for (int k = 0; k < kBtPer; ++k)
@@ -250,25 +259,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // staged page-table entries visible
 
+  // the request's new rows at positions L - T + r, one wave each (a position before the start of the
+  // context, beyond the table width or on a page outside the pool is not written, as the writer skips
+  // such slots)
   if (append) {
-    // the request's new rows at positions L - T + r, quantized and written to the pool by one wave each
-    // (a position before the start of the context, beyond the table width or on a page outside the
-    // pool is not written, as the writer skips such slots); the stores are complete before any gather
-    // (the wait before the row list's barrier)
     for (int r = w; r < a.T; r += kWaves) {
-      u32x4 raw = nraw;
-      uint32_t rope = nrope;
+      RowWords rw = nw;
       if (r >= kWaves) {
         const int64_t nr = (int64_t)b * a.T + r;
-        raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
-        rope = a.new_rope[nr * a.new_rope_stride + lane];
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+        rw = quant_row_words<FMT>(raw, a.new_rope[nr * a.new_rope_stride + lane], lane);
       }
       const int p = L - a.T + r;
       if (p < 0 || (p >> 6) >= npg) continue;
       const int page = staged ? btl[p >> 6] : btg[p >> 6];
       if (page < 0 || page >= a.num_pages) continue;
-      quant_row_wave<FMT>(raw, rope, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB,
-                          lane);
+      store_row_words<FMT>(rw, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB,
+                           lane);
     }
   }
 

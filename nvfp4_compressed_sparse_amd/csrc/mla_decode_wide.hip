@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
         qraw[tt][ks] = *reinterpret_cast<const u32x4*>(qb + (int64_t)16 * tt * kQK + 32 * ks);
   }
 
-  // append (as in the 16/32-head kernel): wave w holds new row w of the request; rows w + 4i, when T > 4,
-  // are loaded where they are written
+  // append (as in the 16/32-head kernel): wave w quantizes new row w of the request while the page table
+  // is in flight and writes it once the table is staged; rows w + 4i, when T > 4, are loaded and
+  // quantized where they are written
   const bool append = a.new_nope != nullptr;
   u32x4 nraw = u32x4{0u, 0u, 0u, 0u};
   uint32_t nrope = 0;
@@ -151,6 +152,11 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
       for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
     }
   }
+  RowWords nw{0u, 0u, 0u};
+  if (append && w < a.T) {
+    nw = quant_row_words<0>(nraw, nrope, lane);
+    asm volatile("" : "+v"(nw.lat0), "+v"(nw.lat1), "+v"(nw.rope));  // keep the quantization here
+  }
   if (bt_regs) {
 #pragma unroll
     for (int k = 0; k < kBtPer; ++k)
@@ -164,18 +170,17 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(DecodeArgs a)
     // the request's new rows at positions L - T + r, written by one wave each (skipped where the writer
     // would skip the slot); complete before any gather (the wait before the row list's barrier)
     for (int r = w; r < a.T; r += kWWaves) {
-      u32x4 raw = nraw;
-      uint32_t rope = nrope;
+      RowWords rw = nw;
       if (r >= kWWaves) {
         const int64_t nr = (int64_t)b * a.T + r;
-        raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
-        rope = a.new_rope[nr * a.new_rope_stride + lane];
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(a.new_nope + nr * a.new_nope_stride + 8 * lane);
+        rw = quant_row_words<0>(raw, a.new_rope[nr * a.new_rope_stride + lane], lane);
       }
       const int p = L - a.T + r;
       if (p < 0 || (p >> 6) >= npg) continue;
       const int page = staged ? btl[p >> 6] : btg[p >> 6];
       if (page < 0 || page >= a.num_pages) continue;
-      quant_row_wave<0>(raw, rope, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB, lane);
+      store_row_words<0>(rw, a.wpool + (uint64_t)page * (uint64_t)a.page_stride + (uint64_t)(p & 63) * ROWB, lane);
     }
   }
 

@@ -335,10 +335,18 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 
 // Quantize-on-write of one token by one wavefront (row formats and rounding as in mla_quant.hip): lane l
 // holds latent elements 8l..8l+7 (raw, the 16-byte load of the bf16 values) and rope element l
-// (rope_bits, bf16), and the wavefront writes the 352- or 576-byte row at dst: 88 or 144 coalesced
-// dwords.
+// (rope_bits, bf16).  quant_row_words computes the lane's dwords of the row in registers, store_row_words
+// writes the 352- or 576-byte row at dst (88 or 144 coalesced dwords), so that a caller can quantize
+// before it knows where the row goes.
+struct RowWords {
+  uint32_t lat0;  // NVFP4: the lane's 8 nibbles (bytes 4l..4l+3); FP8: codes of elements 8l..8l+3
+  uint32_t lat1;  // NVFP4: scale bytes 4l..4l+3 (lanes 0-7); FP8: codes of elements 8l+4..8l+7
+  uint32_t rope;  // rope codes 4l..4l+3 (lanes 0-15)
+};
+
 template <int FMT>
-__device__ __forceinline__ void quant_row_wave(u32x4 raw, uint32_t rope_bits, uint8_t* dst, int lane) {
+__device__ __forceinline__ RowWords quant_row_words(u32x4 raw, uint32_t rope_bits, int lane) {
+  RowWords o;
   const uint32_t rope_code = f32_to_e4m3(bf16_to_f32(rope_bits));
   uint32_t h[8];
 #pragma unroll
@@ -360,25 +368,42 @@ __device__ __forceinline__ void quant_row_wave(u32x4 raw, uint32_t rope_bits, ui
       uint32_t code = ((h[k] >> 12) & 8u) | mag;
       nib |= code << (4 * k);
     }
-    *reinterpret_cast<uint32_t*>(dst + 4 * lane) = nib;
+    o.lat0 = nib;
     // scale bytes: block j lives in lanes 2j and 2j+1; dword q holds blocks 4q..4q+3
     const int src = 8 * (lane & 7);
     uint32_t s0 = __shfl(sc, src, 64), s1 = __shfl(sc, src + 2, 64);
     uint32_t s2 = __shfl(sc, src + 4, 64), s3 = __shfl(sc, src + 6, 64);
-    if (lane < 8) *reinterpret_cast<uint32_t*>(dst + 256 + 4 * lane) = s0 | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    o.lat1 = s0 | (s1 << 8) | (s2 << 16) | (s3 << 24);
   } else {
     uint32_t c[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) c[k] = f32_to_e4m3(bf16_to_f32(h[k]));
-    u32x2 v = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-    *reinterpret_cast<u32x2*>(dst + 8 * lane) = v;
+    o.lat0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    o.lat1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
   }
   // rope bytes: dword q holds rope values 4q..4q+3 (lanes 4q..4q+3)
   const int src = 4 * (lane & 15);
   uint32_t r0 = __shfl(rope_code, src, 64), r1 = __shfl(rope_code, src + 1, 64);
   uint32_t r2 = __shfl(rope_code, src + 2, 64), r3 = __shfl(rope_code, src + 3, 64);
+  o.rope = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+  return o;
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_row_words(const RowWords& o, uint8_t* dst, int lane) {
+  if constexpr (FMT == 0) {
+    *reinterpret_cast<uint32_t*>(dst + 4 * lane) = o.lat0;
+    if (lane < 8) *reinterpret_cast<uint32_t*>(dst + 256 + 4 * lane) = o.lat1;
+  } else {
+    *reinterpret_cast<u32x2*>(dst + 8 * lane) = u32x2{o.lat0, o.lat1};
+  }
   constexpr int kRopeOff = FMT == 0 ? 288 : 512;
-  if (lane < 16) *reinterpret_cast<uint32_t*>(dst + kRopeOff + 4 * lane) = r0 | (r1 << 8) | (r2 << 16) | (r3 << 24);
+  if (lane < 16) *reinterpret_cast<uint32_t*>(dst + kRopeOff + 4 * lane) = o.rope;
+}
+
+template <int FMT>
+__device__ __forceinline__ void quant_row_wave(u32x4 raw, uint32_t rope_bits, uint8_t* dst, int lane) {
+  store_row_words<FMT>(quant_row_words<FMT>(raw, rope_bits, lane), dst, lane);
 }
 
 }  // namespace mla

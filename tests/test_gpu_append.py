@@ -82,11 +82,29 @@ def two_launch(case, d, bt_dev, ctx_dev, idx_dev, full_slots, num_splits):
     return pool, out, lse
 
 
-def fused(case, d, bt_dev, ctx_dev, idx_dev, old_slots, knope, krope, num_splits, pool=None):
+def poison_new_rows(case, pool, ctx, bt):
+    """Fill the bytes where the step's new rows go with 0xFF (an E4M3 NaN in every scale and rope byte),
+    so that a read of a new row that does not see the step's own row shows up in the outputs."""
+    c = case.cfg
+    offs = []
+    for b in range(c.B):
+        for t in range(c.T):
+            p = int(ctx[b]) - c.T + t
+            if p < 0 or p // 64 >= bt.shape[1] or bt[b, p // 64] < 0:
+                continue
+            offs.append(int(bt[b, p // 64]) * c.page_stride + (p % 64) * c.row_bytes)
+    if offs:
+        o = torch.tensor(offs, dtype=torch.int64, device="cuda")
+        pool[(o[:, None] + torch.arange(c.row_bytes, device="cuda")[None, :]).reshape(-1)] = 255
+
+
+def fused(case, d, bt_dev, ctx_dev, idx_dev, old_slots, knope, krope, num_splits, pool=None, poison=None):
     c = case.cfg
     if pool is None:
         pool = torch.zeros(case.pool_bytes, dtype=torch.uint8, device="cuda")
         quant(d, old_slots, pool, case)
+    if poison is not None:
+        poison_new_rows(case, pool, *poison)
     lse = torch.empty((c.B, c.T, c.H), dtype=torch.float32, device="cuda")
     out, _ = M.mla_sparse_decode_append(d["q"], pool, c.page_stride, case.lay.num_pages, bt_dev, ctx_dev, idx_dev,
                                         dev_bf16(knope), dev_bf16(krope), c.sm_scale, causal=c.causal,
@@ -122,6 +140,8 @@ def check_equal(name, a, b):
 CASES = [
     # (B, T, H, topk, causal, splits)
     (2, 1, 16, 256, False, 0),
+    (2, 1, 16, 200, False, 3),  # partial last steps: their padding rows read a new row
+    (2, 2, 32, 200, True, 0),
     (3, 1, 16, 2048, False, 3),
     (2, 4, 16, 256, True, 0),
     (2, 4, 32, 512, True, 2),
@@ -141,7 +161,8 @@ def test_append_matches_two_launches_and_oracle(B, T, H, topk, causal, splits):
     say(f"append B={B} T={T} H={H} topk={topk} causal={causal} splits={splits}")
     d = case.to_device()
     p2, o2, l2 = two_launch(case, d, d["bt"], d["ctx"], d["idx"], full_slots, splits)
-    p1, o1, l1 = fused(case, d, d["bt"], d["ctx"], d["idx"], old_slots, knope, krope, splits)
+    p1, o1, l1 = fused(case, d, d["bt"], d["ctx"], d["idx"], old_slots, knope, krope, splits,
+                       poison=(case.lay.ctx, bt))
     check_equal("pool", p1, p2)
     check_equal("out", o1, o2)
     check_equal("lse", l1, l2)
@@ -168,7 +189,7 @@ def test_append_edges(H):
     d = case.to_device()
     bt_dev = torch.from_numpy(narrow).cuda()
     p2, o2, l2 = two_launch(case, d, bt_dev, d["ctx"], d["idx"], full_slots, 0)
-    p1, o1, l1 = fused(case, d, bt_dev, d["ctx"], d["idx"], old_slots, knope, krope, 0)
+    p1, o1, l1 = fused(case, d, bt_dev, d["ctx"], d["idx"], old_slots, knope, krope, 0, poison=(ctx, narrow))
     check_equal("pool", p1, p2)
     check_equal("out", o1, o2)
     check_equal("lse", l1, l2)
