@@ -47,17 +47,11 @@ def algorithmic_work(cfg, valid_rows: int):
     return rows_bytes + qo_bytes + list_bytes, flops
 
 
-def uses_wide_kernel(cfg) -> bool:
-    """The library serves NVFP4 rows with 64 or 128 heads with its wide-head decode kernel."""
-    return cfg.fmt == "nvfp4" and cfg.H in (64, 128)
-
-
 def source_hash(cfg):
     """Hash of the sources of the decode kernel this workload runs (shared headers and the ABI included)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_compressed_sparse_amd", "csrc")
-    kernel = "mla_decode_wide.hip" if uses_wide_kernel(cfg) else "mla_decode.hip"
-    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", kernel):
+    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", "mla_decode.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -385,15 +379,13 @@ def main():
         roof["kernel"] = ("mla_sparse_decode_pth call: pth_decode_kernel (+ pth_merge_kernel when split), "
                           "back-to-back calls timed with HIP events on their stream")
     elif fused:
-        roof["kernel"] = ("mla_sparse_decode_append call: " +
-                          ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") +
-                          " (the step's new rows quantized and written in its prologue, split merge inside), "
-                          "back-to-back calls timed with HIP events on its stream")
+        roof["kernel"] = ("mla_sparse_decode_append call: decode_kernel (the step's new rows quantized and "
+                          "written in its prologue, split merge inside), back-to-back calls timed with HIP "
+                          "events on its stream")
     else:
         roof["kernel"] = (("mla_sparse_decode_fp8" if sparse_fp8 else "mla_sparse_decode") if cfg.topk
-                          else "mla_dense_decode_fp8") + " call: " + \
-            ("decode_wide_kernel" if uses_wide_kernel(cfg) else "decode_kernel") + \
-            " (split merge inside), back-to-back calls timed with HIP events on its stream"
+                          else "mla_dense_decode_fp8") + \
+            " call: decode_kernel (split merge inside), back-to-back calls timed with HIP events on its stream"
     roof["algorithmic_bytes_per_launch"] = int(bytes_per)
     roof["flops_per_launch"] = flops_per
     roof["launch_us"] = round(dec_avg_us, 3)

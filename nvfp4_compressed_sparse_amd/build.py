@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_nvfp4.so")
 PROBE_LIB = os.path.join(PKG, "libmla_probe.so")  # measurement probes for the benchmark (not the decode path)
-SOURCES = ["mla_quant.hip", "mla_decode.hip", "mla_decode_wide.hip", "mla_stage.hip", "mla_topk.hip", "mla_indexer.hip",
+SOURCES = ["mla_quant.hip", "mla_decode.hip", "mla_stage.hip", "mla_topk.hip", "mla_indexer.hip",
            "mla_pth.hip", "mla_abi.hip", "mla_abi_index.hip", "mla_abi_pth.hip"]
 
 HIPCC_FLAGS = [

@@ -58,21 +58,6 @@ int auto_splits(int64_t units, int64_t entries, int64_t min_splits) {
   return (int)s;
 }
 
-// The wide-head kernel (64 or 128 heads) runs one workgroup per (query token, split) for every head,
-// so one split result is H x 512 values and the merging workgroup reads S-1 of them: its split count
-// stays small (at most 8, and at least 256 list entries per split).
-constexpr int kWideMaxSplits = 8;
-constexpr int kWideMinEntries = 256;
-
-int auto_splits_wide(int64_t units, int64_t entries) {
-  int64_t s = ceil_div(kTargetWorkgroups, units);
-  int64_t cap = ceil_div(entries, kWideMinEntries);
-  if (cap > kWideMaxSplits) cap = kWideMaxSplits;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return (int)s;
-}
-
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout when S > 1: [split arrival counters: a fixed region of kMaxSplitCounters int32, of
@@ -96,11 +81,9 @@ WsLayout workspace_layout(int64_t B, int64_t T, int64_t H, int S) {
 
 // The decode launch for these sizes stays inside the dispatch limits: its grid, in threads, fits 32 bits,
 // and a split launch has at most kMaxSplitCounters arrival counters.
-bool decode_launch_fits(int fmt, int64_t B, int64_t T, int32_t H, int S, bool sparse) {
-  const bool wide = sparse && mla::uses_wide_kernel(fmt, H);
-  const int64_t units = wide ? B * T : B * T * head_groups(H);
-  const int64_t threads = wide ? mla::kWideDecodeThreads : mla::kDecodeThreads;
-  if (units * S * threads > mla::kMaxLaunchThreads) return false;
+bool decode_launch_fits(int64_t B, int64_t T, int32_t H, int S) {
+  const int64_t units = B * T * head_groups(H);
+  if (units * S * mla::kDecodeThreads > mla::kMaxLaunchThreads) return false;
   if (S > 1 && units > mla::kMaxSplitCounters) return false;
   return true;
 }
@@ -167,7 +150,7 @@ int run_decode(int fmt, const void* q, const void* pool, int64_t page_stride, in
   // a dense split starts on a page boundary, so that each 64-row step of the decoder is one page
   if (!indices) chunk = (int)ceil_div(chunk, 64) * 64;
   if (chunk > kMaxChunk) return MLA_ERR_SHAPE;
-  if (!decode_launch_fits(fmt, B, T, H, S, indices != nullptr)) return MLA_ERR_SHAPE;
+  if (!decode_launch_fits(B, T, H, S)) return MLA_ERR_SHAPE;
   size_t need = workspace_for(B, T, H, S);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
@@ -279,7 +262,6 @@ int mla_kv_quant_fp8(const void* k_nope, int64_t nope_stride, const void* k_rope
 
 int mla_sparse_decode_splits(int32_t B, int32_t T, int32_t H, int32_t topk) {
   if (B < 1 || T < 1 || !valid_heads(H) || topk < 1 || topk > MLA_MAX_TOPK) return 0;
-  if (mla::uses_wide_kernel(0, H)) return auto_splits_wide((int64_t)B * T, topk);
   return auto_splits((int64_t)B * T * head_groups(H), topk, 1);
 }
 

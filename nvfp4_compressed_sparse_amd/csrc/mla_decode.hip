@@ -878,7 +878,6 @@ static void launch_one(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream) {
   const bool dense = a.indices == nullptr;
-  if (uses_wide_kernel(fmt, a.H) && !dense) return launch_decode_wide(fmt, a, stream);
   if (fmt == 0) {
     if (dense) return hipErrorInvalidValue;
     if (a.H == 16) launch_one<1, 0, false>(a, stream);

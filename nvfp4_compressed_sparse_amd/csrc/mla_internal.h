@@ -65,8 +65,7 @@ struct StageArgs {
   int32_t* staged_lens;       // [B*T]
 };
 
-constexpr int kDecodeThreads = 512;      // decode_kernel workgroup size
-constexpr int kWideDecodeThreads = 256;  // decode_wide_kernel workgroup size
+constexpr int kDecodeThreads = 512;  // decode_kernel workgroup size
 // A launch's grid, counted in threads, must fit 32 bits (the dispatch packet's grid size).
 constexpr int64_t kMaxLaunchThreads = 0xFFFFFFFFLL;
 // Split arrival counters live in a fixed region at the start of a split decode's workspace, one int32
@@ -77,14 +76,8 @@ constexpr int64_t kMaxSplitCounters = 65536;
 // Tokens one writer call may take: the writers run one 64-lane wave per token.
 constexpr int64_t kMaxWriteTokens = kMaxLaunchThreads / 64;
 
-// Which decode kernel serves a shape: the wide-head kernel for NVFP4 rows with 64 or 128 heads (every
-// row dequantized once for all heads), the 16/32-head-group kernel otherwise.
-inline bool uses_wide_kernel(int fmt, int H) { return fmt == 0 && (H == 64 || H == 128); }
-
 hipError_t launch_quant(int fmt, const QuantArgs& a, hipStream_t stream);
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream);
-// 64 or 128 heads: one workgroup per (query token, split) covers every head (mla_decode_wide.hip).
-hipError_t launch_decode_wide(int fmt, const DecodeArgs& a, hipStream_t stream);
 // The staged path's unpack of each query token's selected NVFP4 rows into FP8 rows (mla_stage.hip).
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 

@@ -148,7 +148,7 @@ CASES = [
     (2, 10, 16, 256, True, 0),  # more new rows than the workgroup has waves
     (2, 1, 64, 256, False, 0),
     (2, 4, 128, 256, True, 2),
-    (1, 6, 128, 512, True, 0),  # more new rows than the wide workgroup has waves
+    (1, 6, 128, 512, True, 0),  # 128 heads: four head groups of one token write the same rows
 ]
 
 

@@ -157,7 +157,7 @@ def test_sparse_decode_tiny_config():
 @pytest.mark.parametrize("H", [32, 128])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 64])
 def test_sparse_decode_split_counts(S, H):
-    # 300 entries: 4 full 64-row steps + a ragged 44 (16/32 heads), 9 full 32-row steps + 12 (64/128)
+    # 300 entries: 4 full 64-row steps + a ragged 44
     case = Case(small(H=H, topk=300, L=5000, seed=13))
     say(f"split count {S} H={H}")
     d = case.to_device()
@@ -178,7 +178,7 @@ def test_softmax_reference_rises(H, pattern, S):
     """Scores that grow along the index list make the running softmax reference rise step after step
     ('rising': about 10 in log2 units per 32 rows; 'steep': about 33) or once at the very end
     ('late_jump': by about 66, 'huge_jump': by about 266), so the accumulated output is rescaled
-    inside the kernel (the 16/32-head kernel rises past 8 log2 units, the 64/128-head kernel past 100).
+    inside the kernel (its reference rises by more than 15 log2 units at a time).
     The query's latent part is zero and its rope part one, so a row's score is sm_scale times the sum
     of its rope values, which the test sets."""
     cfg = small(B=2, H=H, topk=256, L=3000, seed=41)

@@ -38,8 +38,8 @@ def _run(case, d, S, noalloc):
 def test_noalloc_decode_matches_workspace_decode(order):
     big = W.DecodeConfig("na1", B=5, T=1, H=32, topk=1024, fmt="nvfp4", ctx=6000, seed=301)
     small = W.DecodeConfig("na2", B=2, T=2, H=16, topk=300, fmt="nvfp4", ctx=2500, causal=True, seed=302)
-    wide = W.DecodeConfig("na3", B=2, T=1, H=128, topk=700, fmt="nvfp4", ctx=3000, seed=303)
-    runs = [(big, 4), (small, 3), (wide, 2)] if order == "large_then_small" else [(small, 5), (big, 2), (wide, 3)]
+    h128 = W.DecodeConfig("na3", B=2, T=1, H=128, topk=700, fmt="nvfp4", ctx=3000, seed=303)
+    runs = [(big, 4), (small, 3), (h128, 2)] if order == "large_then_small" else [(small, 5), (big, 2), (h128, 3)]
     for cfg, S in runs:
         case = Case(cfg)
         say(f"{order}: {cfg.name} B={cfg.B} T={cfg.T} H={cfg.H} topk={cfg.topk} S={S}")
