@@ -237,3 +237,62 @@ def case_oracle_at(case, ctx, idx):
     c = case.cfg
     return oracle.sparse_decode(case.q, case.oracle_pool(), c.page_stride, case.lay.num_pages, case.lay.block_table,
                                 ctx, idx, c.sm_scale, c.causal, fmt=c.fmt)[:2]
+
+
+@pytest.mark.parametrize("name", ["sparse", "spec", "pages15", "short35"])
+def test_full_size_fused_step_sampled(name):
+    """The fused step at the full sizes bench.py times it (one mla_sparse_decode_append launch with the
+    library's split choice): the cache holds every row but the step's new ones, whose slots are poisoned;
+    after the call every new row is bit-exact against the oracle's writer, and sampled query tokens,
+    which select their request's newest positions, match the oracle."""
+    import oracle
+    from cases import sampled_oracle
+    cfg = W.CONFIGS[name]
+    say(f"full-size fused {name}: generating inputs")
+    inp = W.device_inputs(cfg, "cuda", n_sets=1)
+    lay = inp["layout"]
+    T = cfg.T
+    rows = np.concatenate([inp["row_off"][b] + lay.ctx[b] - T + np.arange(T) for b in range(cfg.B)]).astype(np.int64)
+    rows_d = torch.from_numpy(rows).cuda()
+    old = inp["slots"].clone()
+    old[rows_d] = -1
+    pool = torch.zeros(lay.num_pages * cfg.page_stride, dtype=torch.uint8, device="cuda")
+    inp["pool"] = pool
+    M.mla_kv_quant_nvfp4(inp["lat"], inp["rope"], old, pool, cfg.page_stride, lay.num_pages)
+    new_slots = inp["slots"][rows_d].cpu().numpy()
+    offs = (new_slots // 64) * cfg.page_stride + (new_slots % 64) * cfg.row_bytes
+    gidx = torch.from_numpy((offs[:, None] + np.arange(cfg.row_bytes)[None, :]).reshape(-1)).cuda()
+    pool[gidx] = 255
+    # every query token selects its request's newest positions first
+    idx = inp["idx_sets"][0].cpu().numpy()
+    for b in range(cfg.B):
+        newest = np.arange(int(lay.ctx[b]) - T, int(lay.ctx[b]), dtype=np.int32)
+        for t in range(T):
+            r = idx[b, t]
+            r = r[~np.isin(r, newest)]
+            keep = np.concatenate([newest, r])[: cfg.topk]
+            idx[b, t, :] = -1
+            idx[b, t, : keep.size] = keep
+    idx_d = torch.from_numpy(idx).cuda()
+    q = inp["q_sets"][0]
+    lse = torch.empty((cfg.B, T, cfg.H), dtype=torch.float32, device="cuda")
+    say(f"full-size fused {name}: decode")
+    out, _ = M.mla_sparse_decode_append(q, pool, cfg.page_stride, lay.num_pages, inp["bt"], inp["ctx"], idx_d,
+                                        inp["lat"][rows_d].contiguous(), inp["rope"][rows_d].contiguous(),
+                                        cfg.sm_scale, causal=cfg.causal, lse=lse)
+    torch.cuda.synchronize()
+    grows = pool[gidx].cpu().numpy().reshape(-1, cfg.row_bytes)
+    lat = inp["lat"][rows_d].view(torch.int16).cpu().numpy().view(np.uint16)
+    rope = inp["rope"][rows_d].view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(rows.size):
+        assert np.array_equal(grows[r], oracle.quant_row_nvfp4(lat[r], rope[r])), f"new row {r} differs"
+    nq = cfg.B * T
+    qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed + 7).choice(nq, min(6, nq), replace=False))))
+    say(f"full-size fused {name}: oracle on query tokens {qtoks}")
+    ro, rl, vm, pools_ok = sampled_oracle(cfg, inp, qtoks, idx_d, q)
+    assert pools_ok, "pool rows differ from the oracle's quantization"
+    g = bf16_to_np(out).reshape(nq, cfg.H, 512)[qtoks]
+    gl = lse.cpu().numpy().astype(np.float64).reshape(nq, cfg.H)[qtoks]
+    say(compare_outputs(g, ro, gl, rl, f"full-size fused {name}", vmax=vm))
+    del inp, pool
+    torch.cuda.empty_cache()

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from cases import Case, bf16_to_np, compare_outputs, v_abs_of_rows
+from cases import Case, bf16_to_np, compare_outputs, sampled_oracle, v_abs_of_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -612,55 +612,6 @@ def test_staged_decode_matches_oracle(H):
 
 
 # --------------------------------------------------------------------------- full-size configs, sampled
-def _sampled_oracle(cfg, inp, qtoks, idx_d, q_d):
-    """Oracle results for sampled query tokens of a full-size device case: the selected source rows are
-    copied to the host and quantized by the oracle into a small pool of their own."""
-    lay = inp["layout"]
-    outs, lses, vmaxes, pools_ok = [], [], [], True
-    idx_all = idx_d.cpu().numpy() if idx_d is not None else None
-    q_all = q_d.view(torch.int16).cpu().numpy().view(np.uint16)
-    for qt in qtoks:
-        b, t = divmod(int(qt), cfg.T)
-        L = int(lay.ctx[b])
-        lim = W.position_limit(L, cfg.T, t, cfg.causal)
-        if idx_all is not None:
-            ids = idx_all[b, t]
-            pos = np.unique(ids[(ids >= 0) & (ids <= lim)])
-        else:
-            pos = np.arange(lim + 1)
-        pages = np.unique(pos // 64)
-        mini_bt = np.full((1, lay.block_table.shape[1]), -1, np.int32)
-        mini_bt[0, pages] = np.arange(1, pages.size + 1)
-        rows = torch.from_numpy(inp["row_off"][b] + pos).cuda()
-        lat = inp["lat"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
-        rope = inp["rope"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
-        npg = pages.size + 1
-        pool = np.zeros(npg * cfg.page_stride, np.uint8)
-        slots = (mini_bt[0, pos // 64].astype(np.int64) * 64 + pos % 64)
-        oracle.kv_quant(cfg.fmt, lat, rope, slots, pool, cfg.page_stride, npg)
-        ctx = np.array([L], np.int32)
-        q1 = q_all[b:b + 1]
-        if idx_all is not None:
-            o, l, _ = oracle.sparse_decode(q1, pool, cfg.page_stride, npg, mini_bt, ctx, idx_all[b:b + 1],
-                                           cfg.sm_scale, cfg.causal, units=[t], fmt=cfg.fmt)
-        else:
-            o, l, _ = oracle.dense_decode_fp8(q1, pool, cfg.page_stride, npg, mini_bt, ctx, cfg.sm_scale, cfg.causal,
-                                              units=[t])
-        outs.append(o[0])
-        lses.append(l[0])
-        # the device pool holds the same bytes for these rows
-        gslots = lay.block_table[b, pos // 64].astype(np.int64) * 64 + pos % 64
-        offs = (gslots // 64) * cfg.page_stride + (gslots % 64) * cfg.row_bytes
-        rb = cfg.row_bytes
-        gidx = torch.from_numpy((offs[:, None] + np.arange(rb)[None, :]).reshape(-1)).cuda()
-        grows = inp["pool"][gidx].cpu().numpy().reshape(-1, rb)
-        oidx = (slots // 64) * cfg.page_stride + (slots % 64) * rb
-        orows = pool[(oidx[:, None] + np.arange(rb)[None, :]).reshape(-1)].reshape(-1, rb)
-        pools_ok &= np.array_equal(grows, orows)
-        vmaxes.append(v_abs_of_rows(orows, cfg.fmt).max(0)[None, :] if orows.size else np.zeros((1, 512)))
-    return np.stack(outs), np.stack(lses), np.stack(vmaxes), pools_ok
-
-
 @pytest.mark.parametrize("name", ["sparse", "spec", "mixed", "dense_b4", "dense_b8", "dense_b16", "pages15", "pages20",
                                   "short35", "pages15_fp8"])
 def test_full_size_config_sampled(name):
@@ -690,7 +641,7 @@ def test_full_size_config_sampled(name):
     nq = cfg.B * cfg.T
     qtoks = sorted(set([0, nq - 1] + list(np.random.default_rng(cfg.seed).choice(nq, min(6, nq), replace=False))))
     say(f"full-size {name}: oracle on query tokens {qtoks}")
-    ro, rl, vm, pools_ok = _sampled_oracle(cfg, inp, qtoks, idx, q)
+    ro, rl, vm, pools_ok = sampled_oracle(cfg, inp, qtoks, idx, q)
     assert pools_ok, "pool rows differ from the oracle's quantization"
     g = bf16_to_np(out).reshape(nq, cfg.H, 512)[qtoks]
     gl = lse.cpu().numpy().astype(np.float64).reshape(nq, cfg.H)[qtoks]
