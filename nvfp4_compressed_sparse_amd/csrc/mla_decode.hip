@@ -148,6 +148,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int qtok = rest / a.splits;
   const int b = qtok / a.T, t = qtok % a.T;
   const int h0 = hg * NH;
+  // the request's context length, read before any memory operation the compiler cannot see through
+  // (the DMA below), so that it is a scalar load: a vector load here would be waited for with every
+  // load issued before it, the query DMA included, ahead of the page-table and list loads
+  const int L = a.ctx[b];
 
   // The head group's queries (NH x 576 bf16, contiguous) are staged in LDS by DMA, issued first since
   // they depend on nothing else; the score waves take their fragments from there.  The staging area
@@ -180,7 +184,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   const int e0 = s * a.chunk;
   const int* btg = a.block_table + (int64_t)b * a.bt_stride;
-  const int L = a.ctx[b];
   const int lim = a.causal ? L - a.T + t : L - 1;
   if (tid < 2) sh.flag[tid] = 0;
   // published maxima start at -inf: a raise takes the largest published value, and only waves that
