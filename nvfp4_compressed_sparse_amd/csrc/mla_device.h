@@ -86,24 +86,6 @@ __device__ __forceinline__ float e4m3_code_value(int c) {
   return e == 0 ? sub : nrm;
 }
 
-// Nearest E4M3FN code (0..126) to amax / 6, ties to the even code, saturating at 448.  Binary search
-// over the exact midpoints between neighbouring codes: 6 * (v(k) + v(k+1)) / 2 is exact in fp32.
-__device__ __forceinline__ int e4m3_scale_code_div6(float amax) {
-  int lo = 0, hi = 126;
-#pragma unroll
-  for (int it = 0; it < 7; ++it) {
-    int mid = (lo + hi + 1) >> 1;
-    int k = mid - 1;  // is amax/6 past the midpoint between codes k and k+1?
-    float thr = 3.0f * (e4m3_code_value(k) + e4m3_code_value(k + 1));
-    bool up = (amax > thr) || (amax == thr && ((k + 1) & 1) == 0);
-    if (lo < hi) {
-      if (up) lo = mid;
-      else hi = mid - 1;
-    }
-  }
-  return lo;
-}
-
 // Nearest E4M3FN byte to a finite fp32 value, ties to even, saturating at +-448.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   uint32_t u = __float_as_uint(x);
@@ -119,6 +101,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
     code = (r >> 20) - (120u << 3);
   }
   return sign | code;
+}
+
+// Nearest E4M3FN code (0..126) to amax / 6, ties to the even code, saturating at 448.  The code of the
+// rounded quotient amax * (1/6) is at most one code away (its relative error is below 2^-23, and two
+// exact quotients can only round to different codes across a midpoint); it is then corrected against
+// the exact midpoints 6 * (v(k) + v(k+1)) / 2 = 3 * (v(k) + v(k+1)), which fp32 holds exactly.
+__device__ __forceinline__ int e4m3_scale_code_div6(float amax) {
+  auto rounds_up = [amax](int k) {  // amax / 6 lies past the midpoint between codes k and k+1
+    const float thr = 3.0f * (e4m3_code_value(k) + e4m3_code_value(k + 1));
+    return (amax > thr) || (amax == thr && ((k + 1) & 1) == 0);
+  };
+  int c = (int)(f32_to_e4m3(amax * (1.0f / 6.0f)) & 0x7Fu);
+  if (c <= 125 && rounds_up(c)) ++c;
+  else if (c >= 1 && !rounds_up(c - 1)) --c;
+  return c;
 }
 
 // e2m1 magnitude code (0..7) of a / s, nearest grid point of {0,.5,1,1.5,2,3,4,6}, ties to the even
