@@ -10,13 +10,15 @@
 // converts without overflow; P rounds to FP16.
 //
 // Work decomposition: one 512-thread workgroup (8 wavefronts, two per SIMD) per compute unit.
-//   * workgroup = (query token, head group of 16*HT heads, split s of the token's position list);
-//     the pages split one token's rows over a cluster of 3-8 SMs merged through distributed shared
-//     memory; here the splits are separate workgroups merged by their log-sum-exp weights.
+//   * workgroup = (query token, head group of 16*HT heads, split s of the token's position list); 64
+//     and 128 heads are 2 or 4 head groups; the pages split one token's rows over a cluster of 3-8 SMs
+//     merged through distributed shared memory; here the splits are separate workgroups merged by
+//     their log-sum-exp weights.
 //   * prologue: the page-table entries the split can touch are staged in LDS; the split's list entries
 //     are validated (index < 0, past the causal limit, or on a page-table entry outside the pool ->
 //     dropped, which also skips their loads) and compacted into an LDS list of row addresses (order
-//     kept, so results are deterministic).
+//     kept, so results are deterministic).  In the fused step (mla_sparse_decode_append) the prologue
+//     also quantizes and stores the request's new rows, complete before the first gather.
 //   * rows are consumed in steps of 64; one role's waves gather them by LDS-DMA (16 bytes per lane, no
 //     registers) into a ring of raw row slots, several steps ahead.
 //   * the waves specialise, as the pages' warp groups do: waves 0-3 score, waves 4-7 accumulate, one of
@@ -39,7 +41,7 @@
 //     operations so that each FP16 pair the converter produces is already (row r, row r+1) of one
 //     column.
 //   * epilogue: the score waves' softmax sums go through LDS; the accumulate waves normalize and write
-//     (bf16 output, or fp32 partials for the split merge).
+//     (bf16 output, or FP16 partials and the split's lse for the merge by the last split to finish).
 #include "mla_device.h"
 #include "mla_internal.h"
 
