@@ -406,10 +406,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   };
   // The score waves gather.  Issuing a step's LDS-DMA loads stalls the issuing wave for a while (the
-  // vector memory path takes them at a limited rate); with NVFP4 rows the accumulate waves have the
-  // longer instruction stream (dequantizing V costs more than K's share), so the score waves, which
-  // would otherwise wait at the step barrier, absorb it.  (FP8 rows leave the score waves no such
-  // slack, but neither the accumulate waves nor all eight waves together issue them faster.)
+  // vector memory path takes them at a limited rate); issuing them from the accumulate waves instead
+  // (which then also await them before publishing each step), or from all eight waves, measured slower
+  // for both row formats.
   constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
   constexpr int kEarly = kHeadStart < kFirst ? kHeadStart : kFirst;
   // steps gathered so far (score waves; wave-uniform)

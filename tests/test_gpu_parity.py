@@ -125,6 +125,50 @@ def test_quant_adversarial_rows_bit_exact(fmt):
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
 
 
+def test_quant_every_block_amax_bit_exact():
+    """Every non-negative finite bf16 value as the largest magnitude of a 16-value block (the block scale
+    is the E4M3 code nearest to amax / 6), with the block's other values below it and of either sign:
+    the NVFP4 writer's bytes against the oracle's, and the same rows through the fused step's writes."""
+    vals = np.arange(0, 0x7F80, dtype=np.uint16)  # bit patterns of 0 .. largest finite bf16
+    nblk = vals.size
+    rng = np.random.default_rng(31)
+    amax = W.bf16_to_f32(vals).astype(np.float64)
+    frac = rng.random((nblk, 16))
+    blk = W.bf16_bits((amax[:, None] * frac).astype(np.float32))  # magnitudes at most amax
+    blk = np.where(rng.random((nblk, 16)) < 0.5, blk | 0x8000, blk).astype(np.uint16)
+    blk[np.arange(nblk), rng.integers(0, 16, nblk)] = vals | (rng.integers(0, 2, nblk) << 15).astype(np.uint16)
+    pad = (-nblk) % 32
+    blk = np.concatenate([blk, np.zeros((pad, 16), np.uint16)])
+    lat = blk.reshape(-1, 512)
+    n = lat.shape[0]
+    rope = W.bf16_bits(rng.standard_normal((n, 64)).astype(np.float32))
+    num_pages = (n + 63) // 64 + 1
+    slots = np.arange(n, dtype=np.int64) + 64
+    say(f"every block amax: {nblk} blocks in {n} rows")
+    ref = np.zeros(num_pages * 64 * 352, np.uint8)
+    oracle.kv_quant("nvfp4", lat, rope, slots, ref, 64 * 352, num_pages)
+    pool = torch.zeros(ref.size, dtype=torch.uint8, device="cuda")
+    kn = torch.from_numpy(lat.view(np.int16)).cuda().view(torch.bfloat16)
+    kr = torch.from_numpy(rope.view(np.int16)).cuda().view(torch.bfloat16)
+    M.mla_kv_quant_nvfp4(kn, kr, torch.from_numpy(slots).cuda(), pool, 64 * 352, num_pages)
+    bad = np.nonzero(pool.cpu().numpy() != ref)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+    # the fused step writes the same rows: one request per row, each row its request's newest position
+    # request b has one page-table entry, page 1 + b // 64, and its new row is position b % 64 (context
+    # b % 64 + 1): slot 64 + b, as above
+    B = n
+    ctx = (np.arange(B) % 64 + 1).astype(np.int32)
+    bt = (1 + np.arange(B) // 64).astype(np.int32).reshape(B, 1)
+    q = torch.zeros((B, 1, 16, 576), dtype=torch.bfloat16, device="cuda")
+    idx = torch.full((B, 1, 1), -1, dtype=torch.int32, device="cuda")
+    pool2 = torch.zeros(ref.size, dtype=torch.uint8, device="cuda")
+    M.mla_sparse_decode_append(q, pool2, 64 * 352, num_pages, torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(),
+                               idx, kn, kr, 0.07)
+    torch.cuda.synchronize()
+    bad = np.nonzero(pool2.cpu().numpy() != ref)[0]
+    assert bad.size == 0, f"fused step: {bad.size} bytes differ, first at {bad[:8]}"
+
+
 def test_quant_strided_inputs_from_one_kv_tensor():
     # nope and rope as views of one [n, 576] tensor (stride 576), written through a pool of 2 layers
     rng = np.random.default_rng(21)
