@@ -111,6 +111,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay the step's calls as captured HIP graphs instead of prepared launches")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query tokens in the oracle sample (0 = auto)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="decode kernel phase timeline: run the step on the instrumented build of the library "
+                         "(libmla_nvfp4_timeline.so, the same kernels with phase timestamps compiled in) and print "
+                         "the last launch's phase times (medians over workgroups) instead of the metric line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--op", default="decode", choices=["decode", "index-topk", "index-logits", "dsa-step"],
@@ -143,6 +147,9 @@ def main():
     import torch
     import nvfp4_compressed_sparse_amd as M
 
+    if args.timeline:
+        M.use_timeline_library()
+        args.no_cpu_baseline = args.no_peaks = True
     cfg = W.CONFIGS[args.workload]
     staged_path = args.path == "staged"
     pth_path = args.path == "pth"
@@ -347,6 +354,11 @@ def main():
         f"us/step; decode call avg {dec_avg_us:.2f} us over {args.steps} back-to-back calls")
     if fused:  # the timed steps are themselves back-to-back launches of the one call
         dec_avg_us = ms_per_step * 1e3
+    if args.timeline:
+        if staged_path or pth_path:
+            raise SystemExit("--timeline covers decode_kernel (the native paths)")
+        print_timeline(M, cfg, S, ms_per_step, dec_avg_us, fused)
+        return
 
     nq = cfg.B * cfg.T
     value = nq / (ms_per_step * 1e-3)
@@ -431,6 +443,52 @@ def main():
     if cpu is not None:
         res["cpu_baseline"] = run_cpu_baseline(cfg, cpu)
     print(json.dumps(res), flush=True)
+
+
+TIMELINE_PHASES = [(1, "prologue loads issued (query DMA, list entries, page table; new rows loaded)"),
+                   (2, "loads landed, page table staged (new rows quantized)"),
+                   (3, "row list compacted (new rows stored and complete)"),
+                   (4, "first gathers: step 0 visible"),
+                   (5, "last step done"),
+                   (6, "split result tile normalized"),
+                   (7, "split result stored, arrival counter taken")]
+
+
+def print_timeline(M, cfg, S, ms_per_step, dec_avg_us, fused):
+    """Phase times of the last decode launch from the instrumented library: per workgroup, the stamps of
+    its wave 0 (10 ns ticks) relative to the first workgroup's start; medians and 90th percentiles over the
+    workgroups that reach each phase."""
+    hg = 1 if cfg.H == 16 else cfg.H // 32
+    n = cfg.B * cfg.T * hg * S
+    if n > 4096:
+        raise SystemExit(f"--timeline records at most 4096 workgroups (this launch has {n})")
+    st = M.timeline(n)
+    t0 = st[:, 0].min()
+    rel = (st[:, :9] - t0) * 0.01  # us
+    merged = st[:, 13] == 1
+    rows = [("workgroup start", rel[:, 0])]
+    rows += [(name, rel[st[:, i] != 0, i]) for i, name in TIMELINE_PHASES]
+    rows += [("end, merging workgroups" if S > 1 else "end", rel[merged, 8])]
+    if S > 1:
+        rows += [("end, other workgroups", rel[~merged, 8])]
+    steps = st[:, 15]
+    per_step = (st[:, 5] - st[:, 4]) * 0.01 / np.maximum(steps, 1)
+    out = {"workload": cfg.name, "workgroups": int(n), "splits": S, "steps_per_workgroup": int(np.median(steps)),
+           "launch_us": round(dec_avg_us, 2), "ms_per_step": round(ms_per_step, 6), "fused": fused,
+           "span_us": round(float(rel[:, 8].max()), 2), "step_us_median": round(float(np.median(per_step)), 3),
+           "xcds_per_query_token": None, "phases_us": []}
+    for name, v in rows:
+        if v.size:
+            out["phases_us"].append({"phase": name, "median": round(float(np.median(v)), 2),
+                                     "p90": round(float(np.percentile(v, 90)), 2), "workgroups": int(v.size)})
+    # the XCC each workgroup ran on, grouped by query token (logical index / (head groups * splits))
+    tok = st[:, 14] // (hg * S)
+    out["xcds_per_query_token"] = int(max(len(set(st[tok == q, 12].tolist())) for q in np.unique(tok)))
+    log(f"[bench] timeline of the last launch ({n} workgroups, {S} splits, median "
+        f"{out['steps_per_workgroup']} steps; step {out['step_us_median']} us):")
+    for ph in out["phases_us"]:
+        log(f"[bench]   {ph['phase']:<64s} median {ph['median']:7.2f} us   p90 {ph['p90']:7.2f} us")
+    print(json.dumps({"timeline": out}), flush=True)
 
 
 def measure_achievable(cfg, pool, inp, idx_sets, lay, lim_d):

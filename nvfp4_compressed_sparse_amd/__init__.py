@@ -12,6 +12,7 @@ import ctypes
 import os
 
 from .build import LIB as LIB_PATH
+from .build import TIMELINE_LIB as TIMELINE_LIB_PATH
 from .build import build
 
 LATENT_DIM, ROPE_DIM, QK_DIM, PAGE_TOKENS = 512, 64, 576, 64
@@ -46,7 +47,36 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         build()
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = _load(LIB_PATH)
+    return _lib
+
+
+def use_timeline_library() -> None:
+    """Bind every function to the instrumented build of the library instead (the same kernels with the
+    decode kernel's phase timestamps compiled in; see timeline()).  For bench.py --timeline: call it
+    before any other function of this module."""
+    global _lib
+    if _lib is not None:
+        raise RuntimeError("use_timeline_library() must come before the library is first used")
+    if not os.path.exists(TIMELINE_LIB_PATH):
+        build()
+    _lib = _load(TIMELINE_LIB_PATH, timeline=True)
+
+
+def timeline(workgroups: int):
+    """The instrumented library's phase stamps of the last decode launch: int64 [workgroups, 16]
+    (slots described beside MLA_STAMP in csrc/mla_decode.hip; stamps in 10 ns ticks)."""
+    import numpy as np
+    if _lib is None or not hasattr(_lib, "mla_debug_timeline"):
+        raise RuntimeError("timeline() needs use_timeline_library()")
+    out = np.zeros((workgroups, 16), np.uint64)
+    if _lib.mla_debug_timeline(out.ctypes.data, workgroups) != 0:
+        raise RuntimeError("mla_debug_timeline failed")
+    return out.astype(np.int64)
+
+
+def _load(path, timeline=False) -> ctypes.CDLL:
+    L = ctypes.CDLL(path)
     P, i64, i32, sz, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     sig = {
         "mla_abi_version": (ctypes.c_int, []),
@@ -80,11 +110,12 @@ def lib() -> ctypes.CDLL:
         "mla_index_topk_workspace_bytes": (sz, [i64, i64]),
         "mla_index_topk": (ctypes.c_int, [P, i64, P, i64, i32, P, P, sz, P]),
     }
+    if timeline:
+        sig["mla_debug_timeline"] = (ctypes.c_int, [P, i64])
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
     return L
 
 

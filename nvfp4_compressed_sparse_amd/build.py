@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_nvfp4.so")
 PROBE_LIB = os.path.join(PKG, "libmla_probe.so")  # measurement probes for the benchmark (not the decode path)
+# the decode library again with the decode kernel's phase timestamps compiled in (MLA_TIMELINE): for
+# bench.py --timeline only, never loaded by the product path
+TIMELINE_LIB = os.path.join(PKG, "libmla_nvfp4_timeline.so")
 SOURCES = ["mla_quant.hip", "mla_decode.hip", "mla_stage.hip", "mla_topk.hip", "mla_indexer.hip",
            "mla_pth.hip", "mla_abi.hip", "mla_abi_index.hip", "mla_abi_pth.hip"]
 
@@ -32,14 +35,16 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link the shared libraries (always rebuilds): the decode
-    library and the measurement probes."""
+    library, the measurement probes and the decode library with the phase timeline compiled in."""
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        timeline = src.endswith(":timeline")
+        src = src.split(":")[0]
+        obj = os.path.join(objdir, src.replace(".hip", "_timeline.o" if timeline else ".o"))
+        cmd = [cc, *HIPCC_FLAGS, *(["-DMLA_TIMELINE"] if timeline else []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -47,9 +52,11 @@ def build(verbose: bool = False) -> str:
             print(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        objs = list(ex.map(compile_one, SOURCES + ["mla_probe.hip"]))
-    for lib, parts in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        objs = list(ex.map(compile_one, SOURCES + ["mla_probe.hip", "mla_decode.hip:timeline"]))
+    n = len(SOURCES)
+    timeline_objs = [objs[-1] if s == "mla_decode.hip" else o for s, o in zip(SOURCES, objs[:n])]
+    for lib, parts in ((LIB, objs[:n]), (PROBE_LIB, objs[n:n + 1]), (TIMELINE_LIB, timeline_objs)):
         tmp = lib + ".tmp"
         r = subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *parts, "-o", tmp], capture_output=True,
                            text=True)

@@ -58,6 +58,21 @@ constexpr int kTileStride = kLatent + 4;       // floats per head of a split's r
 constexpr int kPrologueSteps = 3;              // steps gathered before step 0 is awaited
 constexpr int kHeadStart = 2;                  // of those, steps gathered before the query fragments
 
+// Phase timeline, compiled only into the instrumented library (MLA_TIMELINE defined; the decode library
+// has none of it): wave 0 of each workgroup keeps s_memrealtime stamps (a 100 MHz device clock) in
+// scalar registers and writes them once, at its end, so no store or wait is added on the way.
+// Slots: 0 start, 1 prologue loads issued, 2 page table staged, 3 row list complete, 4 step 0 visible,
+// 5 last step done, 6 split result tile complete, 7 arrival counter taken, 8 end; 12 XCC id, 13 merged
+// (1 for the workgroup that merged, or for an unsplit one), 14 logical workgroup index, 15 steps.
+#ifdef MLA_TIMELINE
+constexpr int kTimelineSlots = 16;
+constexpr int kTimelineWGs = 4096;
+__device__ uint64_t g_timeline[kTimelineWGs * kTimelineSlots];
+#define MLA_STAMP(i) (stamp[(i)] = __builtin_amdgcn_s_memrealtime())
+#else
+#define MLA_STAMP(i) ((void)0)
+#endif
+
 // Geometry of the raw-row ring: steps of 64 rows; each of the four score waves gathers 16 rows of each
 // step (see the kernel for why the score waves).  In LDS a row
 // takes one 16-byte chunk more than it holds (368 or 592 bytes), so that the rows read by the 16 lanes
@@ -141,6 +156,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int g = lane >> 4, n = lane & 15;
   const bool scorer = w < 4;
   const int r4 = w & 3;  // score waves: row tile; accumulate waves: column quarter
+#ifdef MLA_TIMELINE
+  uint64_t stamp[kTimelineSlots] = {};
+  MLA_STAMP(0);
+#endif
 
   const int HG = a.H / NH;
   const int j = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -249,6 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       for (int k = 0; k < EPT; ++k) pos[k] = ebase + k < e1 ? ip[k] : -1;
     }
   }
+  MLA_STAMP(1);
   RowWords nw{0u, 0u, 0u};
   if (append && w < a.T) {
     nw = quant_row_words<FMT>(nraw, nrope, lane);
@@ -263,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int i = tid; i < npg; i += kThreads) btl[i] = btg[i];
   }
   __syncthreads();  // staged page-table entries visible
+  MLA_STAMP(2);
 
   // the request's new rows at positions L - T + r, one wave each (a position before the start of the
   // context, beyond the table width or on a page outside the pool is not written, as the writer skips
@@ -335,6 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // every load issued so far (indices, page table, the query DMA) has landed before the gathers start
   wait_vmem();
   __syncthreads();  // row list and staged queries complete; the page-table staging area is free again
+  MLA_STAMP(3);
   }
 
   const int nsteps = (n_valid + kStepRows - 1) / kStepRows;
@@ -463,6 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     issue_upto(kFirst - 1);
     wait_for_step(0);
     lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
+    MLA_STAMP(4);
     const int rt = r4;
     float lsum[HT];
 #pragma unroll
@@ -591,6 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       if (g == 0) sh.wsum[16 * tt + n][rt] = l;
     }
     wait_vmem();
+    MLA_STAMP(5);
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
@@ -800,6 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int64_t hrow = (int64_t)qtok * a.H + h0 + h;
     const float* own = tile + h * kTileStride + c4;
     __syncthreads();  // the result tile and its lse are complete
+    MLA_STAMP(6);
     {
       uint64_t* dst = reinterpret_cast<uint64_t*>(a.part_o + (hrow * S + s) * kLatent + c4);
 #pragma unroll
@@ -813,6 +838,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     int* counter = a.counters + ((int64_t)qtok * HG + hg);
     if (tid == 0) sh.last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
+    MLA_STAMP(7);
     if (sh.last) {
       // running merge over the splits in their order, four per round with every load of a round (results
       // and lse) issued together; this workgroup's own split comes from LDS, rounded to FP16 as the
@@ -871,6 +897,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+#ifdef MLA_TIMELINE
+  MLA_STAMP(8);
+  stamp[12] = (uint64_t)__builtin_amdgcn_s_getreg(20 | (3 << 11));  // HW_REG_XCC_ID, bits 3:0
+  stamp[13] = S == 1 ? 1u : (uint64_t)sh.last;
+  stamp[14] = (uint64_t)j;
+  stamp[15] = (uint64_t)nsteps;
+  if (tid == 0 && blockIdx.x < (unsigned)kTimelineWGs) {
+#pragma unroll
+    for (int i = 0; i < kTimelineSlots; ++i) g_timeline[blockIdx.x * kTimelineSlots + i] = stamp[i];
+  }
+#endif
 }
 
 template <int HT, int FMT, bool DENSE>
@@ -879,6 +916,16 @@ static void launch_one(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.B * a.T * HG * a.splits);
   hipLaunchKernelGGL((decode_kernel<HT, FMT, DENSE>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
+
+#ifdef MLA_TIMELINE
+// The instrumented library's stamps of the last decode launch, workgroups [0, n) (n <= 4096), 16 per
+// workgroup; returns 0 on success.
+extern "C" int mla_debug_timeline(uint64_t* host, int64_t n) {
+  if (!host || n < 1 || n > kTimelineWGs) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), (size_t)n * kTimelineSlots * 8, 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 1;
+}
+#endif
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream) {
   const bool dense = a.indices == nullptr;

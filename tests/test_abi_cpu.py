@@ -27,6 +27,17 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(M.EXPORTS)
 
 
+def test_timeline_library_exports_the_decode_abi_and_its_reader():
+    from nvfp4_compressed_sparse_amd.build import TIMELINE_LIB
+    T = ctypes.CDLL(TIMELINE_LIB)
+    for n in _declared_functions() + _declared_functions("mla_timeline.h"):
+        assert hasattr(T, n), n
+    assert _declared_functions("mla_timeline.h") == ["mla_debug_timeline"]
+    assert not hasattr(M.lib(), "mla_debug_timeline")  # the product library has no instrumentation
+    T.mla_debug_timeline.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    assert T.mla_debug_timeline(None, 1) == 1 and T.mla_debug_timeline(FAKE, 4097) == 1  # rejected on the host
+
+
 def test_probe_library_exports_every_declared_symbol():
     from nvfp4_compressed_sparse_amd import probe
     names = _declared_functions("mla_probe.h")
