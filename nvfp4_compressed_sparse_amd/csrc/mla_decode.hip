@@ -169,10 +169,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int qtok = rest / a.splits;
   const int b = qtok / a.T, t = qtok % a.T;
   const int h0 = hg * NH;
-  // the request's context length, read before any memory operation the compiler cannot see through
-  // (the DMA below), so that it is a scalar load: a vector load here would be waited for with every
-  // load issued before it, the query DMA included, ahead of the page-table and list loads
-  const int L = a.ctx[b];
+  // The request's context length.  Dense: read here, before any memory operation the compiler cannot
+  // see through (the DMA below), so that it is a scalar load, needed at once.  Sparse: loaded after the
+  // list and page-table loads, since it is first needed once the table is staged; read here, its
+  // dependent round trip was waited for before those loads went out (scalar loads return out of
+  // order, so the wait for any kernel argument loaded after it waited for it too).
+  int L = DENSE ? a.ctx[b] : 0;
 
   // The head group's queries (NH x 576 bf16, contiguous) are staged in LDS by DMA, issued first since
   // they depend on nothing else; the score waves take their fragments from there.  The staging area
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   const int e0 = s * a.chunk;
   const int* btg = a.block_table + (int64_t)b * a.bt_stride;
-  const int lim = a.causal ? L - a.T + t : L - 1;
+  int lim = a.causal ? L - a.T + t : L - 1;  // (sparse: set again below, once L is loaded)
   if (tid < 2) sh.flag[tid] = 0;
   // published maxima start at -inf: a raise takes the largest published value, and only waves that
   // raise publish (every score a wave saw before stays within 2^15 of the reference it left behind)
@@ -269,6 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
   MLA_STAMP(1);
+  int ctx_v = a.ctx[b];  // a vector load (it follows the DMA), awaited after the page-table barrier
   RowWords nw{0u, 0u, 0u};
   if (append && w < a.T) {
     nw = quant_row_words<FMT>(nraw, nrope, lane);
@@ -284,6 +287,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // staged page-table entries visible
   MLA_STAMP(2);
+  asm("" : "+v"(ctx_v));  // used from here on, as a vector value: no wait for it before this point
+  L = ctx_v;
+  lim = a.causal ? L - a.T + t : L - 1;
 
   // the request's new rows at positions L - T + r, one wave each (a position before the start of the
   // context, beyond the table width or on a page outside the pool is not written, as the writer skips
