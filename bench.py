@@ -458,11 +458,11 @@ def print_timeline(M, cfg, S, ms_per_step, dec_avg_us, fused):
     """Phase times of the last decode launch from the instrumented library: per workgroup, the stamps of
     its wave 0 (10 ns ticks) relative to the first workgroup's start; medians and 90th percentiles over the
     workgroups that reach each phase."""
-    hg = 1 if cfg.H == 16 else cfg.H // 32
-    n = cfg.B * cfg.T * hg * S
+    n = int(M.timeline(1)[0, 11])  # the launch's workgroups (16- or 32-head groups, or 64 at 64/128 heads)
     if n > 4096:
         raise SystemExit(f"--timeline records at most 4096 workgroups (this launch has {n})")
     st = M.timeline(n)
+    hg = n // (cfg.B * cfg.T * S)
     t0 = st[:, 0].min()
     rel = (st[:, :9] - t0) * 0.01  # us
     merged = st[:, 13] == 1

@@ -149,7 +149,8 @@ size_t mla_dense_decode_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t
  *   lse           (device) fp32 [B, T, H] or NULL
  *   workspace     (device) >= mla_sparse_decode_workspace_bytes(...) bytes, 256-byte aligned, zero-filled
  *                 before its first use (see above); may be NULL when that size is 0
- * The grid is B*T*(H/32, or 1 at H = 16)*S workgroups of 512 threads; it must stay below 2^32 threads.
+ * The grid is B*T*(H/32, or 1 at H = 16)*S workgroups of 512 threads (at H = 64 or 128 unsplit, with
+ * B*T*H/64 >= 256: B*T*H/64 workgroups of 64 heads); it must stay below 2^32 threads.
  */
 int mla_sparse_decode(const void* q, const void* pool, int64_t page_stride_bytes, int64_t num_pages,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,

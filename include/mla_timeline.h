@@ -7,8 +7,9 @@
  * clock, 10 ns ticks) in scalar registers and writes them once, at its end, to a device array of 4,096
  * workgroups x 16 slots, indexed by the hardware workgroup index.  Slots: 0 start, 1 prologue loads issued,
  * 2 page table staged, 3 row list complete, 4 step 0 visible, 5 last step done, 6 split result tile
- * complete, 7 arrival counter taken, 8 end (0 where the workgroup's path has no such phase); 12 the XCC
- * the workgroup ran on, 13 1 if it merged the splits or was unsplit, 14 its logical index, 15 its steps.
+ * complete, 7 arrival counter taken, 8 end (0 where the workgroup's path has no such phase); 11 the
+ * launch's workgroup count, 12 the XCC the workgroup ran on, 13 1 if it merged the splits or was unsplit,
+ * 14 its logical index, 15 its steps.
  * Each launch overwrites the slots of its workgroups; workgroups past the first 4,096 are not recorded.
  */
 #ifndef MLA_TIMELINE_H

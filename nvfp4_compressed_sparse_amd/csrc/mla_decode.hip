@@ -11,7 +11,9 @@
 //
 // Work decomposition: one 512-thread workgroup (8 wavefronts, two per SIMD) per compute unit.
 //   * workgroup = (query token, head group of 16*HT heads, split s of the token's position list); 64
-//     and 128 heads are 2 or 4 head groups; the pages split one token's rows over a cluster of 3-8 SMs
+//     and 128 heads are 2 or 4 groups of 32 heads, or, unsplit with enough query tokens, 1 or 2 groups
+//     of 64 (HT = 4: each K and V fragment dequantized once for twice the heads); the pages split one
+//     token's rows over a cluster of 3-8 SMs
 //     merged through distributed shared memory; here the splits are separate workgroups merged by
 //     their log-sum-exp weights.
 //   * prologue: the page-table entries the split can touch are staged in LDS; the split's list entries
@@ -62,8 +64,9 @@ constexpr int kHeadStart = 2;                  // of those, steps gathered befor
 // has none of it): wave 0 of each workgroup keeps s_memrealtime stamps (a 100 MHz device clock) in
 // scalar registers and writes them once, at its end, so no store or wait is added on the way.
 // Slots: 0 start, 1 prologue loads issued, 2 page table staged, 3 row list complete, 4 step 0 visible,
-// 5 last step done, 6 split result tile complete, 7 arrival counter taken, 8 end; 12 XCC id, 13 merged
-// (1 for the workgroup that merged, or for an unsplit one), 14 logical workgroup index, 15 steps.
+// 5 last step done, 6 split result tile complete, 7 arrival counter taken, 8 end; 11 the launch's
+// workgroups, 12 XCC id, 13 merged (1 for the workgroup that merged, or for an unsplit one), 14 logical
+// workgroup index, 15 steps.
 #ifdef MLA_TIMELINE
 constexpr int kTimelineSlots = 16;
 constexpr int kTimelineWGs = 4096;
@@ -79,8 +82,9 @@ __device__ uint64_t g_timeline[kTimelineWGs * kTimelineSlots];
 // of a lane group start on 16 different 4-bank groups (the stride is 28 or 20 dwords mod 64).  Lane l
 // of a wave's DMA load u fills LDS chunk 64u+l of the wave's 16 rows; the padding chunks are not
 // loaded.  A step's slot is reused NS steps later; step k is issued during step k-(NS-2).  Sparse FP8
-// lists keep three slots: with the row list beside it, a fourth 37 KB slot would not fit in LDS.
-template <int FMT, bool DENSE>
+// lists keep three slots: with the row list beside it, a fourth 37 KB slot would not fit in LDS; a
+// 64-head workgroup keeps five NVFP4 slots beside its larger P tiles.
+template <int FMT, bool DENSE, int NH>
 struct Geo {
   static constexpr int kRowBytes = FMT == 0 ? kNvfp4Row : kFp8Row;
   static constexpr int kChunks = kRowBytes / 16;                 // 22 or 36 per row
@@ -90,7 +94,7 @@ struct Geo {
   static constexpr int kLoads = (kWaveChunks + 63) / 64;         // 6 or 10 DMA loads per wave per step
   static_assert((kLoads - 1) * 64 < kWaveChunks, "only a wave's last gather load is partial");
   static constexpr int kSlot = kStepRows * kStride;              // bytes of one step
-  static constexpr int kSlots = FMT == 0 ? 6 : (DENSE ? 4 : 3);  // ring depth
+  static constexpr int kSlots = FMT == 0 ? (NH > 32 ? 5 : 6) : (DENSE ? 4 : 3);  // ring depth
   static constexpr int kRing = kSlots * kSlot;
 };
 
@@ -111,7 +115,7 @@ __device__ __forceinline__ void write_p(uint8_t* prow, int rt, int g, const floa
 // split (64-aligned, so that each step is one page) keeps its page-table entries instead.
 template <int FMT, int NH, bool DENSE>
 struct Shared {
-  uint8_t ring[Geo<FMT, DENSE>::kRing];
+  uint8_t ring[Geo<FMT, DENSE, NH>::kRing];
   uint8_t ptile[2][NH * kPStride];             // P of steps k (even/odd): [head][row], FP16
   uint32_t rowlist[DENSE ? 1 : kMaxChunk];     // sparse: row addresses of the split's valid entries
   int pages[DENSE ? kMaxChunk / kStepRows : 1];  // dense: page of each step, -1 = not in the pool
@@ -127,12 +131,13 @@ struct Shared {
 
 // The new reference of every head after a raise, from the score waves' maxima of the step (identical
 // in every wave: same inputs).  Returns the factor that rescales sums taken against the old one.
+// The wave holds head tiles tb..tb+HT-1.
 template <int HT, int NH>
-__device__ __forceinline__ void raise_reference(const float (&smax)[NH][4], int n, float (&ref)[HT],
+__device__ __forceinline__ void raise_reference(const float (&smax)[NH][4], int n, int tb, float (&ref)[HT],
                                                 float (&alpha)[HT]) {
 #pragma unroll
   for (int tt = 0; tt < HT; ++tt) {
-    const int h = 16 * tt + n;
+    const int h = 16 * (tb + tt) + n;
     const float ms = fmaxf(fmaxf(smax[h][0], smax[h][1]), fmaxf(smax[h][2], smax[h][3]));
     const float rnew = ms - ref[tt] > kLazyRescale ? ms : ref[tt];
     alpha[tt] = ref[tt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ref[tt] - rnew);
@@ -142,7 +147,7 @@ __device__ __forceinline__ void raise_reference(const float (&smax)[NH][4], int 
 
 template <int HT, int FMT, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
-  using G = Geo<FMT, DENSE>;
+  using G = Geo<FMT, DENSE, 16 * HT>;
   constexpr int ROWB = G::kRowBytes;
   constexpr int RS = G::kStride;
   constexpr int NL = G::kLoads;
@@ -156,6 +161,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int g = lane >> 4, n = lane & 15;
   const bool scorer = w < 4;
   const int r4 = w & 3;  // score waves: row tile; accumulate waves: column quarter
+  // Score-wave tiles: at 16 and 32 heads a score wave takes one 16-row tile of each step for every head;
+  // at 64 heads (HT = 4) two row tiles for half of the heads, so that each K fragment it dequantizes
+  // feeds two head tiles, as at 32 heads, and its query fragments stay at 32 heads' worth of registers.
+  constexpr int SRT = HT > 2 ? 2 : 1;   // row tiles per score wave
+  constexpr int SHT = HT > 2 ? 2 : HT;  // head tiles per score wave
+  const int rt0 = HT > 2 ? 2 * (r4 & 1) : r4;   // its first row tile
+  const int ht0 = HT > 2 ? 2 * (r4 >> 1) : 0;   // its first head tile
 #ifdef MLA_TIMELINE
   uint64_t stamp[kTimelineSlots] = {};
   MLA_STAMP(0);
@@ -179,10 +191,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // The head group's queries (NH x 576 bf16, contiguous) are staged in LDS by DMA, issued first since
   // they depend on nothing else; the score waves take their fragments from there.  The staging area
   // is the part of the ring the first gathers leave alone (slots NS-2 and NS-1).
-  constexpr int kQBytes = NH * kQK * 2;
+  // (64 heads: each score wave loads and converts its own 32 heads' fragments instead, below)
+  constexpr int kQBytes = HT > 2 ? 0 : NH * kQK * 2;
   static_assert(kQBytes <= 2 * G::kSlot, "query staging must fit in two ring slots");
   uint8_t* qstage = sh.ring + (NS - 2) * G::kSlot;
-  {
+  if constexpr (HT <= 2) {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)qtok * a.H + h0) * kQK);
 #pragma unroll
     for (int u = 0; u < (kQBytes / 1024 + kWaves - 1) / kWaves; ++u) {
@@ -190,7 +203,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       if (blk < kQBytes / 1024) dma16(qsrc + 1024 * blk + 16 * lane, qstage + 1024 * blk);
     }
   }
-
   // The fused step (new rows given): wave w quantizes new row w of the request (the bf16 input, loaded
   // with the prologue's loads) while the page table and the list entries are in flight, and stores it
   // once the table is staged; rows w + 8i, when T > 8, are loaded and quantized there.  The stores are
@@ -458,14 +470,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
   // a split's normalized result tile, [NH][kTileStride] fp32, reuses the ring after the main loop
   float* tile = reinterpret_cast<float*>(sh.ring);
-  static_assert(NH * kTileStride * 4 <= G::kRing, "result tile must fit in the ring");
+  // (64-head workgroups run unsplit only: the host launches them with S = 1, and they have no tile)
+  static_assert(HT > 2 || NH * kTileStride * 4 <= G::kRing, "result tile must fit in the ring");
   float ref[HT];  // softmax reference per head 16tt+n (base 2), identical in every wave
 #pragma unroll
   for (int tt = 0; tt < HT; ++tt) ref[tt] = -INFINITY;
-  const int S = a.splits;
+  const int S = HT > 2 ? 1 : a.splits;
 
   if (scorer) {
-    // ================= score waves: S^T = K q^T, P = 2^(s - ref) for rows 16rt..16rt+15 of step k
+    // ================= score waves: S^T = K q^T, P = 2^(s - ref) for their rows of step k: row tiles
+    // rt0..rt0+SRT-1 (16 rows each), head tiles ht0..ht0+SHT-1
     // The first kPrologueSteps steps (at most NS-2) are gathered before step 0 is awaited, kHeadStart of
     // them before the query fragments are formed and the rest after; the remainder of the prefetch
     // window follows once step 0 has landed.  With every workgroup of the launch gathering at once, a
@@ -474,115 +488,151 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
     issue_upto(kEarly - 1);
     lds_barrier();  // the FP16 query tile and the heads' shifts are in LDS (matches the accumulate waves' barrier)
-    // query fragments (B operand), FP16: lane (g, n) holds head 16tt+n, latent dims 128g+8ks..+7
-    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17), read from the tile the accumulate waves
-    // converted (each head scaled by its power of two 2^kq); the head's score scale is scaled by 2^-kq.
-    f16x8 qf[HT][18];
-    float sl2h[HT];  // softmax scale * log2(e) * 2^-kq of head 16tt+n
+    // query fragments (B operand), FP16: lane (g, n) holds head 16(ht0+tt)+n, latent dims 128g+8ks..+7
+    // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17), each head scaled by its power of two
+    // 2^kq (the head's score scale is scaled by 2^-kq): read from the tile the accumulate waves
+    // converted, or, at 64 heads (the tile would not fit beside the ring), loaded and converted here
+    // by the wave itself: the four lane groups hold a head's 576 values, so its largest magnitude is a
+    // four-lane maximum.  These loads are waited for together with the first two steps' gathers, which
+    // costs nothing at 64 heads: the steps are long enough that the later gathers still land in time.
+    f16x8 qf[SHT][18];
+    float sl2h[SHT];  // softmax scale * log2(e) * 2^-kq of head 16(ht0+tt)+n
 #pragma unroll
-    for (int tt = 0; tt < HT; ++tt) {
-      sl2h[tt] = __builtin_ldexpf(a.scale_log2, -sh.qshift[16 * tt + n]);
+    for (int tt = 0; tt < SHT; ++tt) {
+      if constexpr (HT > 2) {
+        u32x4 qr[18];
+        const uint16_t* qh = a.q + ((int64_t)qtok * a.H + h0 + 16 * (ht0 + tt) + n) * kQK;
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-        qf[tt][ks] = *reinterpret_cast<const f16x8*>(qstage + 2 * ((16 * tt + n) * kQK + d));
+        for (int ks = 0; ks < 18; ++ks) {
+          const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
+          qr[ks] = *reinterpret_cast<const u32x4*>(qh + d);
+        }
+        uint32_t mq = 0;
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          const uint32_t m = bf16x8_max_mag(qr[ks]);
+          mq = mq > m ? mq : m;
+        }
+        const int kq = q_shift(group4_max_u32(mq));
+        sl2h[tt] = __builtin_ldexpf(a.scale_log2, -kq);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks)
+          qf[tt][ks] = as_f16x8(bf16x2_pow2_to_f16x2(qr[ks][0], kq), bf16x2_pow2_to_f16x2(qr[ks][1], kq),
+                                bf16x2_pow2_to_f16x2(qr[ks][2], kq), bf16x2_pow2_to_f16x2(qr[ks][3], kq));
+      } else {
+        sl2h[tt] = __builtin_ldexpf(a.scale_log2, -sh.qshift[16 * tt + n]);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
+          qf[tt][ks] = *reinterpret_cast<const f16x8*>(qstage + 2 * ((16 * tt + n) * kQK + d));
+        }
       }
     }
     issue_upto(kFirst - 1);
     wait_for_step(0);
     lds_barrier();  // step 0 visible (matches the accumulate waves' first barrier); q staging is free
     MLA_STAMP(4);
-    const int rt = r4;
-    float lsum[HT];
+    float sref[SHT];  // this wave's copy of the reference of its heads (the same in every wave)
+    float lsum[SRT][SHT];
 #pragma unroll
-    for (int tt = 0; tt < HT; ++tt) lsum[tt] = 0.0f;
+    for (int tt = 0; tt < SHT; ++tt) {
+      sref[tt] = -INFINITY;
+#pragma unroll
+      for (int ri = 0; ri < SRT; ++ri) lsum[ri][tt] = 0.0f;
+    }
 
     for (int k = 0; k <= nsteps; ++k) {
       issue_upto(k + NS - 2);  // up to the slot of step k-2 (fully consumed)
-      float sv[HT][4];  // scores times the head's scale (base 2); masked rows -inf
-      float psum[HT];   // sum of this lane's speculative P per head tile
+      float sv[SRT][SHT][4];  // scores times the head's scale (base 2); masked rows -inf
+      float psum[SRT][SHT];   // sum of this lane's speculative P per row tile and head tile
       if (k < nsteps) {
-        const uint8_t* rr = slot_ptr(k) + (16 * rt + n) * RS;
-        f32x4 acc[HT];
-#pragma unroll
-        for (int tt = 0; tt < HT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (FMT == 0) {
-          u32x4 nib[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) nib[q] = *reinterpret_cast<const u32x4*>(rr + 64 * g + 16 * q);
-          const u32x2 sc = *reinterpret_cast<const u32x2*>(rr + 256 + 8 * g);
-          const f16x2 s2[4] = {e4m3x2_to_f16<false>(sc[0]), e4m3x2_to_f16<true>(sc[0]), e4m3x2_to_f16<false>(sc[1]),
-                               e4m3x2_to_f16<true>(sc[1])};
-#pragma unroll
-          for (int ks = 0; ks < 16; ++ks) {
-            const uint32_t d = nib[ks >> 2][ks & 3];
-            const _Float16 shv = ((ks >> 1) & 1) ? s2[ks >> 2].y : s2[ks >> 2].x;
-            const f16x2 ss = {shv, shv};
-            const f16x8 A = as_f16x8(fp4x2_to_f16<0>(d) * ss, fp4x2_to_f16<1>(d) * ss, fp4x2_to_f16<2>(d) * ss,
-                                     fp4x2_to_f16<3>(d) * ss);
-#pragma unroll
-            for (int tt = 0; tt < HT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][ks], acc[tt]);
-          }
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < 16; ++ks) {
-            const u32x2 wv = *reinterpret_cast<const u32x2*>(rr + 128 * g + 8 * ks);
-            const f16x8 A = as_f16x8(e4m3x2_to_f16<false>(wv[0]), e4m3x2_to_f16<true>(wv[0]),
-                                     e4m3x2_to_f16<false>(wv[1]), e4m3x2_to_f16<true>(wv[1]));
-#pragma unroll
-            for (int tt = 0; tt < HT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][ks], acc[tt]);
-          }
-        }
-        {
-          const u32x4 rp = *reinterpret_cast<const u32x4*>(rr + (FMT == 0 ? 288 : 512) + 16 * g);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint32_t w0 = rp[2 * ks], w1 = rp[2 * ks + 1];
-            const f16x8 A = as_f16x8(e4m3x2_to_f16<false>(w0), e4m3x2_to_f16<true>(w0), e4m3x2_to_f16<false>(w1),
-                                     e4m3x2_to_f16<true>(w1));
-#pragma unroll
-            for (int tt = 0; tt < HT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][16 + ks], acc[tt]);
-          }
-        }
-        // scores of rows 16rt+4g+i, heads 16tt+n; base-2 maxima; speculative P = 2^(scale*s - ref) with
-        // the current ref.  Only the last step can hold rows past the list (its padding): masked -inf.
-        // The scaled score is rounded once (no fused multiply-add) and both the maxima and P use that
-        // rounded value, and the reference test compares a difference: so P <= 2^15 holds exactly even
-        // where scores are large enough for an added 8 to round away.
-        const int rbase = k * kStepRows + 16 * rt + 4 * g;
         // (dense: a step whose page is not in the pool selects nothing)
         const bool page_ok = !DENSE || sh.pages[DENSE ? k : 0] >= 0;
         const bool full = (k + 1) * kStepRows <= n_valid && page_ok;
         bool raise = false;
-        float mxs[HT];
+        float mxs[SRT][SHT];
 #pragma unroll
-        for (int tt = 0; tt < HT; ++tt)
+        for (int ri = 0; ri < SRT; ++ri) {
+          const int rt = rt0 + ri;
+          const uint8_t* rr = slot_ptr(k) + (16 * rt + n) * RS;
+          f32x4 acc[SHT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[tt][i] = __fmul_rn(acc[tt][i], sl2h[tt]);
-        if (!full) {
+          for (int tt = 0; tt < SHT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (FMT == 0) {
+            u32x4 nib[4];
 #pragma unroll
-          for (int tt = 0; tt < HT; ++tt)
+            for (int q = 0; q < 4; ++q) nib[q] = *reinterpret_cast<const u32x4*>(rr + 64 * g + 16 * q);
+            const u32x2 sc = *reinterpret_cast<const u32x2*>(rr + 256 + 8 * g);
+            const f16x2 s2[4] = {e4m3x2_to_f16<false>(sc[0]), e4m3x2_to_f16<true>(sc[0]),
+                                 e4m3x2_to_f16<false>(sc[1]), e4m3x2_to_f16<true>(sc[1])};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (rbase + i >= n_valid || !page_ok) sv[tt][i] = -INFINITY;
-        }
+            for (int ks = 0; ks < 16; ++ks) {
+              const uint32_t d = nib[ks >> 2][ks & 3];
+              const _Float16 shv = ((ks >> 1) & 1) ? s2[ks >> 2].y : s2[ks >> 2].x;
+              const f16x2 ss = {shv, shv};
+              const f16x8 A = as_f16x8(fp4x2_to_f16<0>(d) * ss, fp4x2_to_f16<1>(d) * ss, fp4x2_to_f16<2>(d) * ss,
+                                       fp4x2_to_f16<3>(d) * ss);
 #pragma unroll
-        for (int tt = 0; tt < HT; ++tt) {
-          mxs[tt] = max4(sv[tt][0], sv[tt][1], sv[tt][2], sv[tt][3]);
-          raise |= mxs[tt] - ref[tt] > kLazyRescale;
-          const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
-          float p[4];
+              for (int tt = 0; tt < SHT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][ks], acc[tt]);
+            }
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
-          psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
-          write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
+            for (int ks = 0; ks < 16; ++ks) {
+              const u32x2 wv = *reinterpret_cast<const u32x2*>(rr + 128 * g + 8 * ks);
+              const f16x8 A = as_f16x8(e4m3x2_to_f16<false>(wv[0]), e4m3x2_to_f16<true>(wv[0]),
+                                       e4m3x2_to_f16<false>(wv[1]), e4m3x2_to_f16<true>(wv[1]));
+#pragma unroll
+              for (int tt = 0; tt < SHT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][ks], acc[tt]);
+            }
+          }
+          {
+            const u32x4 rp = *reinterpret_cast<const u32x4*>(rr + (FMT == 0 ? 288 : 512) + 16 * g);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const uint32_t w0 = rp[2 * ks], w1 = rp[2 * ks + 1];
+              const f16x8 A = as_f16x8(e4m3x2_to_f16<false>(w0), e4m3x2_to_f16<true>(w0),
+                                       e4m3x2_to_f16<false>(w1), e4m3x2_to_f16<true>(w1));
+#pragma unroll
+              for (int tt = 0; tt < SHT; ++tt) acc[tt] = mfma16x16x32(A, qf[tt][16 + ks], acc[tt]);
+            }
+          }
+          // scores of rows 16rt+4g+i, heads 16(ht0+tt)+n; base-2 maxima; speculative P = 2^(scale*s - ref)
+          // with the current ref.  Only the last step can hold rows past the list (its padding): masked
+          // -inf.  The scaled score is rounded once (no fused multiply-add) and both the maxima and P use
+          // that rounded value, and the reference test compares a difference: so P <= 2^15 holds exactly
+          // even where scores are large enough for an added 8 to round away.
+          const int rbase = k * kStepRows + 16 * rt + 4 * g;
+#pragma unroll
+          for (int tt = 0; tt < SHT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[ri][tt][i] = __fmul_rn(acc[tt][i], sl2h[tt]);
+          if (!full) {
+#pragma unroll
+            for (int tt = 0; tt < SHT; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (rbase + i >= n_valid || !page_ok) sv[ri][tt][i] = -INFINITY;
+          }
+#pragma unroll
+          for (int tt = 0; tt < SHT; ++tt) {
+            mxs[ri][tt] = max4(sv[ri][tt][0], sv[ri][tt][1], sv[ri][tt][2], sv[ri][tt][3]);
+            raise |= mxs[ri][tt] - sref[tt] > kLazyRescale;
+            const float mr = sref[tt] == -INFINITY ? 0.0f : sref[tt];
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[ri][tt][i] - mr);
+            psum[ri][tt] = (p[0] + p[1]) + (p[2] + p[3]);
+            write_p(sh.ptile[k & 1] + (16 * (ht0 + tt) + n) * kPStride, rt, g, p);
+          }
         }
         if (__any(raise)) {  // rare: publish this wave's per-head maxima and raise the flag
 #pragma unroll
-          for (int tt = 0; tt < HT; ++tt) {
-            const float mx = group4_max(mxs[tt]);
-            if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = mx;
-          }
+          for (int ri = 0; ri < SRT; ++ri)
+#pragma unroll
+            for (int tt = 0; tt < SHT; ++tt) {
+              const float mx = group4_max(mxs[ri][tt]);
+              if (g == 0) sh.smax[k & 1][16 * (ht0 + tt) + n][rt0 + ri] = mx;
+            }
           if (lane == 0) sh.flag[k & 1] = 1;
         }
       }
@@ -590,41 +640,50 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       lds_barrier();  // step k's P, flag and maxima, step k+1's rows visible
       if (k < nsteps) {
         if (sh.flag[k & 1]) {  // rare: the reference rises; every wave takes this branch
-          float alpha[HT];
-          raise_reference<HT, NH>(sh.smax[k & 1], n, ref, alpha);
+          float alpha[SHT];
+          raise_reference<SHT, NH>(sh.smax[k & 1], n, ht0, sref, alpha);
 #pragma unroll
-          for (int tt = 0; tt < HT; ++tt) {
-            lsum[tt] *= alpha[tt];
-            const float mr = ref[tt] == -INFINITY ? 0.0f : ref[tt];
-            float p[4];
+          for (int tt = 0; tt < SHT; ++tt) {
+            const float mr = sref[tt] == -INFINITY ? 0.0f : sref[tt];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mr);
-            psum[tt] = (p[0] + p[1]) + (p[2] + p[3]);
-            write_p(sh.ptile[k & 1] + (16 * tt + n) * kPStride, rt, g, p);
+            for (int ri = 0; ri < SRT; ++ri) {
+              lsum[ri][tt] *= alpha[tt];
+              float p[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[ri][tt][i] - mr);
+              psum[ri][tt] = (p[0] + p[1]) + (p[2] + p[3]);
+              write_p(sh.ptile[k & 1] + (16 * (ht0 + tt) + n) * kPStride, rt0 + ri, g, p);
+            }
           }
           lds_barrier();  // rewritten P visible; every wave has read the flag and the maxima
           // the maxima buffer of this parity starts over at -inf for its next use (step k+2)
           if (tid == 0) sh.flag[k & 1] = 0;
 #pragma unroll
-          for (int tt = 0; tt < HT; ++tt)
-            if (g == 0) sh.smax[k & 1][16 * tt + n][rt] = -INFINITY;
+          for (int ri = 0; ri < SRT; ++ri)
+#pragma unroll
+            for (int tt = 0; tt < SHT; ++tt)
+              if (g == 0) sh.smax[k & 1][16 * (ht0 + tt) + n][rt0 + ri] = -INFINITY;
         }
 #pragma unroll
-        for (int tt = 0; tt < HT; ++tt) lsum[tt] += psum[tt];
+        for (int ri = 0; ri < SRT; ++ri)
+#pragma unroll
+          for (int tt = 0; tt < SHT; ++tt) lsum[ri][tt] += psum[ri][tt];
       }
     }
     // softmax sums per head over this wave's rows
 #pragma unroll
-    for (int tt = 0; tt < HT; ++tt) {
-      const float l = group4_sum(lsum[tt]);
-      if (g == 0) sh.wsum[16 * tt + n][rt] = l;
-    }
+    for (int ri = 0; ri < SRT; ++ri)
+#pragma unroll
+      for (int tt = 0; tt < SHT; ++tt) {
+        const float l = group4_sum(lsum[ri][tt]);
+        if (g == 0) sh.wsum[16 * (ht0 + tt) + n][rt0 + ri] = l;
+      }
     wait_vmem();
     MLA_STAMP(5);
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
-  {
+  if constexpr (HT <= 2) {
     // The query tile converted to FP16 in place, each head scaled by its power-of-two shift (from the
     // largest magnitude of its 576 values), here while the score waves issue their first gathers: the 256
     // lanes of the four accumulate waves split the heads, 256 / NH lanes per head, each lane taking every
@@ -766,7 +825,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     lds_barrier();  // matches the score waves' barrier of step k
     if (k < nsteps && sh.flag[k & 1]) {
       float alpha[HT];
-      raise_reference<HT, NH>(sh.smax[k & 1], n, ref, alpha);
+      raise_reference<HT, NH>(sh.smax[k & 1], n, 0, ref, alpha);
 #pragma unroll
       for (int tt = 0; tt < HT; ++tt)
 #pragma unroll
@@ -905,6 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   }
 #ifdef MLA_TIMELINE
   MLA_STAMP(8);
+  stamp[11] = (uint64_t)gridDim.x;
   stamp[12] = (uint64_t)__builtin_amdgcn_s_getreg(20 | (3 << 11));  // HW_REG_XCC_ID, bits 3:0
   stamp[13] = S == 1 ? 1u : (uint64_t)sh.last;
   stamp[14] = (uint64_t)j;
@@ -937,7 +997,10 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream) {
   const bool dense = a.indices == nullptr;
   if (fmt == 0) {
     if (dense) return hipErrorInvalidValue;
-    if (a.H == 16) launch_one<1, 0, false>(a, stream);
+    // 64 or 128 heads, unsplit, with at least one workgroup per compute unit at 64 heads per workgroup:
+    // 64-head groups (each K and V fragment dequantized once for twice the heads); otherwise 32
+    if (a.H >= 64 && a.splits == 1 && (int64_t)a.B * a.T * (a.H / 64) >= 256) launch_one<4, 0, false>(a, stream);
+    else if (a.H == 16) launch_one<1, 0, false>(a, stream);
     else launch_one<2, 0, false>(a, stream);
   } else if (dense) {
     if (a.H == 16) launch_one<1, 1, true>(a, stream);

@@ -149,6 +149,7 @@ CASES = [
     (2, 1, 64, 256, False, 0),
     (2, 4, 128, 256, True, 2),
     (1, 6, 128, 512, True, 0),  # 128 heads: four head groups of one token write the same rows
+    (32, 4, 128, 256, True, 1),  # 256 workgroups of 64 heads: the 64-head workgroup writes and decodes
 ]
 
 

@@ -462,6 +462,78 @@ def test_query_outside_fp16_range_matches_oracle(fmt, H, topk):
                                 vmax=vm))
 
 
+# --------------------------------------------------------------------------- 64-head workgroups
+# Unsplit NVFP4 launches at 64 or 128 heads with at least 256 workgroups of 64 heads run the 64-head
+# workgroup (each score wave takes two 16-row tiles for half of the heads and converts its own query
+# rows).  Its results match the oracle on sampled query tokens, and the 32-head workgroup bit for bit:
+# a smaller batch of the same requests (unsplit, too few tokens for 64-head workgroups) runs that one,
+# and a token's results do not depend on the rest of the batch.
+@pytest.mark.parametrize("H,B,T,topk,L,causal", [(128, 32, 4, 300, 1000, True), (64, 256, 1, 77, 400, False),
+                                                 (128, 128, 1, 2048, 2100, False)])
+def test_sparse_decode_64_head_groups(H, B, T, topk, L, causal):
+    cfg = small(B=B, T=T, H=H, topk=topk, L=L, causal=causal, seed=180 + H + topk)
+    case = Case(cfg)
+    rng = np.random.default_rng(181)
+    idx = case.idx
+    idx[0, :, : topk // 3] = -1            # a run of unused entries
+    idx[1, 0, rng.choice(topk, topk // 4, replace=False)] = -1
+    idx[2, 0, :5] = 10 ** 8                # beyond the context
+    idx[3, :, :] = -1                      # an empty selection
+    case.lay.block_table[4, 1] = case.lay.num_pages + 3  # a page outside the pool
+    assert M.mla_sparse_decode_splits(B, T, H, topk) == 1 and B * T * (H // 64) >= 256
+    say(f"64-head workgroups: H={H} B={B} T={T} topk={topk}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d)
+    n = B * T
+    units = np.unique(np.concatenate([[0, 1, 2, 3 * T, 4 * T, n - 1], rng.choice(n, 10, replace=False)]))
+    ro, rl = case.oracle_decode(units=units)
+    say(compare_outputs(out[units], ro, lse[units], rl, f"64-head H={H} sampled", vmax=case.vmax()[units]))
+    assert not out[3 * T:4 * T].any() and np.all(lse[3 * T:4 * T] == -np.inf)
+    # the 32-head workgroup on the first nb requests
+    nb = max(1, (255 // (T * (H // 64))))
+    lse2 = torch.empty((nb, T, H), dtype=torch.float32, device="cuda")
+    out2, _ = M.mla_sparse_decode(d["q"][:nb], d["pool"], cfg.page_stride, case.lay.num_pages, d["bt"][:nb],
+                                  d["ctx"][:nb], d["idx"][:nb], cfg.sm_scale, causal=causal, num_splits=1, lse=lse2)
+    torch.cuda.synchronize()
+    out2 = bf16_to_np(out2).reshape(nb * T, H, 512)
+    assert np.array_equal(out2, out[:nb * T]), "64-head and 32-head workgroups differ"
+    assert np.array_equal(lse2.cpu().numpy().reshape(nb * T, H), lse[:nb * T])
+    # a query scaled by 2^k with sm_scale * 2^-k: bit-identical (each head's own power-of-two shift)
+    for k in (-100, 100):
+        o3, l3 = gpu_decode(case, d, q=_q_device(_q_times_pow2(case.q, k)), sm_scale=cfg.sm_scale * 2.0 ** -k)
+        assert np.array_equal(o3, out) and np.array_equal(l3, lse), f"q * 2^{k} differs"
+    say(f"64-head H={H}: bit-identical to the 32-head workgroup on {nb * T} tokens and for q * 2^k")
+
+
+def test_sparse_decode_64_head_groups_extreme_queries():
+    """Queries far outside FP16's range in the 64-head workgroup (its score waves convert their own
+    query rows): whole heads at 1e30 and at 1e-30 with bf16 subnormals, against the oracle."""
+    cfg = small(B=32, T=4, H=128, topk=256, L=800, seed=190)
+    case = Case(cfg)
+    q = W.bf16_to_f32(case.q).astype(np.float64)
+    g = np.arange(cfg.H) % 2
+    q[:, :, g == 0, :] *= 1.0e30
+    q[:, :, g == 1, :] *= 1.0e-30
+    q[:, :, g == 1, ::7] *= 1.0e-9
+    qbits = W.bf16_bits(q.astype(np.float32))
+    assert np.isfinite(W.bf16_to_f32(qbits)).all()
+    d = case.to_device()
+    gpu_pool(case, d)
+    case.q = qbits
+    dq = _q_device(qbits)
+    units = np.array([0, 5, 17, 64, 127])
+    vm = case.vmax()[units]
+    for grp, sm in ((0, 1.0 / 2.4e31), (1, 1.0 / 2.4e-29)):
+        out, lse = gpu_decode(case, d, q=dq, sm_scale=sm)
+        ro, rl, _ = oracle.sparse_decode(qbits, case.oracle_pool(), cfg.page_stride, case.lay.num_pages,
+                                         case.lay.block_table, case.lay.ctx, case.idx, sm, units=units)
+        sel = g == grp
+        assert np.isfinite(out[units][:, sel]).all() and np.isfinite(lse[units][:, sel]).all()
+        say(compare_outputs(out[units][:, sel], ro[:, sel], lse[units][:, sel], rl[:, sel], f"64-head group {grp}",
+                            vmax=vm))
+
+
 # --------------------------------------------------------------------------- dense FP8 decode
 @pytest.mark.parametrize("T,causal,S", [(1, False, 0), (1, False, 1), (2, True, 0), (1, False, 7)])
 def test_dense_fp8_decode(T, causal, S):
