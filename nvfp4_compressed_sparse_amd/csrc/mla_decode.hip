@@ -44,6 +44,8 @@
 //     column.
 //   * epilogue: the score waves' softmax sums go through LDS; the accumulate waves normalize and write
 //     (bf16 output, or FP16 partials and the split's lse for the merge by the last split to finish).
+#include <cstddef>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -189,13 +191,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   int L = DENSE ? a.ctx[b] : 0;
 
   // The head group's queries (NH x 576 bf16, contiguous) are staged in LDS by DMA, issued first since
-  // they depend on nothing else; the score waves take their fragments from there.  The staging area
-  // is the part of the ring the first gathers leave alone (slots NS-2 and NS-1).
-  // (64 heads: each score wave loads and converts its own 32 heads' fragments instead, below)
-  constexpr int kQBytes = HT > 2 ? 0 : NH * kQK * 2;
-  static_assert(kQBytes <= 2 * G::kSlot, "query staging must fit in two ring slots");
-  uint8_t* qstage = sh.ring + (NS - 2) * G::kSlot;
-  if constexpr (HT <= 2) {
+  // they depend on nothing else; the accumulate waves convert them in place and the score waves take
+  // their fragments from there.  The staging area is the part of LDS the first gathers leave alone: ring
+  // slots kQSlot.. (the last two at 16/32 heads; at 64 heads, whose 73.7 KB tile is read once per
+  // workgroup instead of once per score wave, the last three and the P tiles after them, with two steps
+  // gathered before step 0 is awaited).
+  constexpr int kQSlot = HT > 2 ? 2 : NS - 2;
+  constexpr int kQBytes = NH * kQK * 2;
+  using SharedT = Shared<FMT, NH, DENSE>;
+  static_assert(offsetof(SharedT, ptile) == G::kRing, "the P tiles follow the ring");
+  static_assert(kQSlot * G::kSlot + kQBytes <= (HT > 2 ? G::kRing + 2 * NH * kPStride : G::kRing),
+                "query staging must fit in the slots the first gathers leave alone");
+  uint8_t* qstage = sh.ring + kQSlot * G::kSlot;
+  {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)qtok * a.H + h0) * kQK);
 #pragma unroll
     for (int u = 0; u < (kQBytes / 1024 + kWaves - 1) / kWaves; ++u) {
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // with coalesced loads while the context length and the split's list entries load at the same
   // time: one memory round trip instead of two or three dependent ones.
   const int npg = (int)a.bt_stride;
-  constexpr int kBtCap = (NS - 2) * G::kSlot / 4;  // below the query staging area
+  constexpr int kBtCap = kQSlot * G::kSlot / 4;  // below the query staging area
   const bool staged = npg <= kBtCap;
   int* btl = reinterpret_cast<int*>(sh.ring);
   constexpr int kBtPer = 6;  // entries per thread loaded before any is stored (tables up to 3,072 pages)
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   // vector memory path takes them at a limited rate); issuing them from the accumulate waves instead
   // (which then also await them before publishing each step), or from all eight waves, measured slower
   // for both row formats.
-  constexpr int kFirst = kPrologueSteps < NS - 2 ? kPrologueSteps : NS - 2;
+  constexpr int kFirst = kPrologueSteps < kQSlot ? kPrologueSteps : kQSlot;
   constexpr int kEarly = kHeadStart < kFirst ? kHeadStart : kFirst;
   // steps gathered so far (score waves; wave-uniform)
   int issued = 0;
@@ -480,52 +488,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   if (scorer) {
     // ================= score waves: S^T = K q^T, P = 2^(s - ref) for their rows of step k: row tiles
     // rt0..rt0+SRT-1 (16 rows each), head tiles ht0..ht0+SHT-1
-    // The first kPrologueSteps steps (at most NS-2) are gathered before step 0 is awaited, kHeadStart of
+    // The first kPrologueSteps steps (at most kQSlot) are gathered before step 0 is awaited, kHeadStart of
     // them before the query fragments are formed and the rest after; the remainder of the prefetch
     // window follows once step 0 has landed.  With every workgroup of the launch gathering at once, a
     // deeper first window makes the memory system interleave the steps, so that step 0 completes only
     // when nearly all of them have; the staggered issue lets the first steps' requests queue first.
-    // The query staging slots (NS-2, NS-1) are not touched before every score wave holds its fragments.
+    // The query staging area (slots kQSlot..) is not touched before every score wave holds its fragments.
     issue_upto(kEarly - 1);
     lds_barrier();  // the FP16 query tile and the heads' shifts are in LDS (matches the accumulate waves' barrier)
     // query fragments (B operand), FP16: lane (g, n) holds head 16(ht0+tt)+n, latent dims 128g+8ks..+7
     // (ks < 16) and rope dims 512+16g+8(ks-16)..+7 (ks = 16, 17), each head scaled by its power of two
     // 2^kq (the head's score scale is scaled by 2^-kq): read from the tile the accumulate waves
-    // converted, or, at 64 heads (the tile would not fit beside the ring), loaded and converted here
-    // by the wave itself: the four lane groups hold a head's 576 values, so its largest magnitude is a
-    // four-lane maximum.  These loads are waited for together with the first two steps' gathers, which
-    // costs nothing at 64 heads: the steps are long enough that the later gathers still land in time.
+    // converted.
     f16x8 qf[SHT][18];
     float sl2h[SHT];  // softmax scale * log2(e) * 2^-kq of head 16(ht0+tt)+n
 #pragma unroll
     for (int tt = 0; tt < SHT; ++tt) {
-      if constexpr (HT > 2) {
-        u32x4 qr[18];
-        const uint16_t* qh = a.q + ((int64_t)qtok * a.H + h0 + 16 * (ht0 + tt) + n) * kQK;
+      const int hq = 16 * (ht0 + tt) + n;
+      sl2h[tt] = __builtin_ldexpf(a.scale_log2, -sh.qshift[hq]);
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-          qr[ks] = *reinterpret_cast<const u32x4*>(qh + d);
-        }
-        uint32_t mq = 0;
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const uint32_t m = bf16x8_max_mag(qr[ks]);
-          mq = mq > m ? mq : m;
-        }
-        const int kq = q_shift(group4_max_u32(mq));
-        sl2h[tt] = __builtin_ldexpf(a.scale_log2, -kq);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks)
-          qf[tt][ks] = as_f16x8(bf16x2_pow2_to_f16x2(qr[ks][0], kq), bf16x2_pow2_to_f16x2(qr[ks][1], kq),
-                                bf16x2_pow2_to_f16x2(qr[ks][2], kq), bf16x2_pow2_to_f16x2(qr[ks][3], kq));
-      } else {
-        sl2h[tt] = __builtin_ldexpf(a.scale_log2, -sh.qshift[16 * tt + n]);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
-          qf[tt][ks] = *reinterpret_cast<const f16x8*>(qstage + 2 * ((16 * tt + n) * kQK + d));
-        }
+      for (int ks = 0; ks < 18; ++ks) {
+        const int d = ks < 16 ? 128 * g + 8 * ks : 512 + 16 * g + 8 * (ks - 16);
+        qf[tt][ks] = *reinterpret_cast<const f16x8*>(qstage + 2 * (hq * kQK + d));
       }
     }
     issue_upto(kFirst - 1);
@@ -683,13 +667,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     __syncthreads();  // sums visible (matches the accumulate waves' barrier below)
   } else {
   // ================= accumulate waves: O^T += V^T P^T for step k-1, columns 128cq..128cq+127
-  if constexpr (HT <= 2) {
+  {
     // The query tile converted to FP16 in place, each head scaled by its power-of-two shift (from the
     // largest magnitude of its 576 values), here while the score waves issue their first gathers: the 256
     // lanes of the four accumulate waves split the heads, 256 / NH lanes per head, each lane taking every
     // (256/NH)-th 16-byte word of the head's 72 (it reads, then rewrites, only its own words).
-    constexpr int LPH = 256 / NH;                          // lanes per head: 8 or 16
-    constexpr int CPL = (kQK / 8 + LPH - 1) / LPH;         // words per lane: 9, or 5 (the last partial)
+    constexpr int LPH = 256 / NH;                          // lanes per head: 4, 8 or 16
+    constexpr int CPL = (kQK / 8 + LPH - 1) / LPH;         // words per lane: 18, 9, or 5 (the last partial)
     const int la = (w - 4) * 64 + lane;
     const int hq = la / LPH, part = la % LPH;
     uint8_t* qh = qstage + 2 * hq * kQK;

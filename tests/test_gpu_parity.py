@@ -211,6 +211,35 @@ def test_sparse_decode_split_counts(S, H):
     say(compare_outputs(out, ro, lse, rl, f"S={S} H={H}", vmax=case.vmax()))
 
 
+def test_workspace_zero_filled_once_serves_calls_of_any_shape():
+    """The workspace rule of the header: zero-filled before its first use, then reused without clearing
+    by calls of different sizes, head counts, split counts and row formats.  Each call's output and lse
+    are bit-identical to the same call with a freshly zeroed workspace (and so within the oracle's
+    tolerance, which the other tests check)."""
+    shapes = [dict(B=4, H=32, topk=300, S=4), dict(B=2, H=16, topk=700, S=8), dict(B=3, H=128, topk=300, S=2),
+              dict(B=1, H=64, topk=513, S=3), dict(B=4, H=32, topk=300, S=4, fmt="fp8"), dict(B=4, H=32, topk=300, S=4)]
+    need = max((M.mla_sparse_decode_fp8_workspace_bytes if s.get("fmt") == "fp8" else
+                M.mla_sparse_decode_workspace_bytes)(s["B"], 1, s["H"], s["topk"], s["S"]) for s in shapes)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, s in enumerate(shapes):
+        fmt = s.get("fmt", "nvfp4")
+        case = Case(small(B=s["B"], H=s["H"], topk=s["topk"], L=5000, fmt=fmt, seed=60 + i))
+        say(f"shared workspace call {i}: {s}")
+        d = case.to_device()
+        gpu_pool(case, d)
+        c = case.cfg
+        fn = M.mla_sparse_decode if fmt == "nvfp4" else M.mla_sparse_decode_fp8
+        res = []
+        for ws in (shared, None):
+            lse = torch.empty((c.B, 1, c.H), dtype=torch.float32, device="cuda")
+            out, _ = fn(d["q"], d["pool"], c.page_stride, case.lay.num_pages, d["bt"], d["ctx"], d["idx"], c.sm_scale,
+                        num_splits=s["S"], lse=lse, workspace=ws)
+            torch.cuda.synchronize()
+            res.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+        assert np.array_equal(res[0][0], res[1][0]), f"call {i}: output differs with the reused workspace"
+        assert np.array_equal(res[0][1], res[1][1]), f"call {i}: lse differs with the reused workspace"
+
+
 def _bf16_bits(x):
     return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
@@ -464,10 +493,10 @@ def test_query_outside_fp16_range_matches_oracle(fmt, H, topk):
 
 # --------------------------------------------------------------------------- 64-head workgroups
 # Unsplit NVFP4 launches at 64 or 128 heads with at least 256 workgroups of 64 heads run the 64-head
-# workgroup (each score wave takes two 16-row tiles for half of the heads and converts its own query
-# rows).  Its results match the oracle on sampled query tokens, and the 32-head workgroup bit for bit:
-# a smaller batch of the same requests (unsplit, too few tokens for 64-head workgroups) runs that one,
-# and a token's results do not depend on the rest of the batch.
+# workgroup (each score wave takes two 16-row tiles for half of the heads; the 64 heads' queries are
+# staged in LDS once per workgroup).  Its results match the oracle on sampled query tokens, and the
+# 32-head workgroup bit for bit: a smaller batch of the same requests (unsplit, too few tokens for
+# 64-head workgroups) runs that one, and a token's results do not depend on the rest of the batch.
 @pytest.mark.parametrize("H,B,T,topk,L,causal", [(128, 32, 4, 300, 1000, True), (64, 256, 1, 77, 400, False),
                                                  (128, 128, 1, 2048, 2100, False)])
 def test_sparse_decode_64_head_groups(H, B, T, topk, L, causal):
