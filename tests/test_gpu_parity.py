@@ -577,6 +577,19 @@ def test_dense_fp8_decode(T, causal, S):
     say(compare_outputs(out, ro, lse, rl, f"dense T={T} S={S}", vmax=case.vmax()))
 
 
+@pytest.mark.parametrize("H,S", [(64, 0), (64, 3), (32, 0), (16, 2)])
+def test_dense_fp8_decode_heads(H, S):
+    """Dense FP8 decode at 64, 32 and 16 heads (two 32-head groups, one group), unsplit and split."""
+    cfg = small(B=3, T=1, H=H, topk=0, fmt="fp8", L=1300, seed=43 + H)
+    case = Case(cfg, ctx=[1300, 700, 65])
+    say(f"dense fp8 H={H} S={S}")
+    d = case.to_device()
+    gpu_pool(case, d)
+    out, lse = gpu_decode(case, d, num_splits=S)
+    ro, rl = case.oracle_decode()
+    say(compare_outputs(out, ro, lse, rl, f"dense H={H} S={S}", vmax=case.vmax()))
+
+
 def test_dense_fp8_pages_outside_the_pool():
     """Page-table entries outside [0, num_pages) select nothing: in the middle of a context, on its
     last (partial) page, and for a split that holds only such pages."""
