@@ -48,10 +48,11 @@ def algorithmic_work(cfg, valid_rows: int):
 
 
 def source_hash(cfg):
-    """Hash of the sources of the decode kernel this workload runs (shared headers and the ABI included)."""
+    """Hash of the sources of the decode kernel this workload runs (shared headers, the ABI and the build
+    script with its compile flags included)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_compressed_sparse_amd", "csrc")
-    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", "mla_decode.hip"):
+    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", "mla_decode.hip", "../build.py"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

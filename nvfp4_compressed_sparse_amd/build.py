@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source flags.  The decode kernels are scheduled with LLVM's iterative ILP strategy: measured
+# against the default (same-box A/B, two rounds each) 211 vs 223 us for the 128-head mixed decode,
+# 62.1 vs 65.8 us for the 128-head dense FP8 decode, and equal or slightly faster at 16/32 heads.
+SOURCE_FLAGS = {"mla_decode.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc() -> str:
@@ -44,7 +48,8 @@ def build(verbose: bool = False) -> str:
         timeline = src.endswith(":timeline")
         src = src.split(":")[0]
         obj = os.path.join(objdir, src.replace(".hip", "_timeline.o" if timeline else ".o"))
-        cmd = [cc, *HIPCC_FLAGS, *(["-DMLA_TIMELINE"] if timeline else []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *(["-DMLA_TIMELINE"] if timeline else []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
