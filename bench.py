@@ -48,13 +48,16 @@ def algorithmic_work(cfg, valid_rows: int):
 
 
 def source_hash(cfg):
-    """Hash of the sources of the decode kernel this workload runs (shared headers, the ABI and the build
-    script with its compile flags included)."""
+    """Hash of the sources of the decode kernel this workload runs (shared headers and the ABI included)
+    and of the compile flags of its source (include paths left out: they differ between machines)."""
+    from nvfp4_compressed_sparse_amd.build import HIPCC_FLAGS, SOURCE_FLAGS
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_compressed_sparse_amd", "csrc")
-    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", "mla_decode.hip", "../build.py"):
+    for f in ("mla_abi.hip", "mla_device.h", "mla_internal.h", "mla_decode.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    flags = [x for x in HIPCC_FLAGS if not os.path.isabs(x)] + SOURCE_FLAGS.get("mla_decode.hip", [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
